@@ -1,0 +1,147 @@
+"""GPU parity of the Q2_0 GEMV / batched GEMV against the CPU oracle, through
+the C ABI.
+
+Bar: every output within 2 BF16 ulp or 1e-2 x row RMS of the oracle; batched
+rows bit-identical to the M=1 launch (page "gemv_q2_vec.rs", doc of
+q2_0_gemv_vec_batchm); the exact-integer regime bit-identical to the oracle;
+rows past M and columns past N never written.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from parity import (CANARY, check_parity, dev_u8, q2_0_gpu, requires_gpu, ulp_histogram)
+from weight_quantized_decode_block_amd import inputs as gen
+from weight_quantized_decode_block_amd import wqd
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "q2_0_closed_forms.json")
+
+
+def _case(wid, N, K, M, salt=0):
+    A = gen.activations(wid, K, M, salt)
+    codes, d = gen.q2_0_weights(wid, N, K, salt)
+    return A, codes, d, wqd.q2_0_pack(codes, d)
+
+
+def _m1_rows(A, packed_dev, N, K):
+    return np.concatenate([q2_0_gpu(A[m:m + 1], packed_dev, N, K, single=True) for m in range(A.shape[0])])
+
+
+def test_small_gemv_parity(oracle_mod):
+    """N=256, K=1024, M=1 (the small Q2_0 workload)."""
+    A, codes, d, packed = _case(1, 256, 1024, 1)
+    got = q2_0_gpu(A, packed, 256, 1024, single=True)
+    ref = oracle_mod.q2_0_gemv(A, codes, d)
+    check_parity(got, ref, "q2_0 256x1024")
+    print("ulp histogram", ulp_histogram(got, ref))
+
+
+def test_qkv_gemv_parity(oracle_mod):
+    """N=K=5120, M=1."""
+    A, codes, d, packed = _case(2, 5120, 5120, 1)
+    got = q2_0_gpu(A, packed, 5120, 5120, single=True)
+    ref = oracle_mod.q2_0_gemv(A, codes, d)
+    check_parity(got, ref, "q2_0 5120^2 M=1")
+    print("ulp histogram", ulp_histogram(got, ref))
+
+
+@pytest.mark.parametrize("M", [2, 4, 5, 8, 16])
+def test_batched_rows_bit_identical_and_parity(oracle_mod, M):
+    """N=K=5120, M in {2,4,5,8,16}; M=16 runs as two 8-row launches."""
+    A, codes, d, packed = _case(3, 5120, 5120, M)
+    Bd = dev_u8(packed)
+    got = q2_0_gpu(A, Bd, 5120, 5120, extra_rows=1)
+    assert np.all(got[M] == CANARY)
+    got = got[:M]
+    assert np.array_equal(got, _m1_rows(A, Bd, 5120, 5120))
+    check_parity(got, oracle_mod.q2_0_gemv(A, codes, d), f"q2_0 5120^2 M={M}")
+
+
+@pytest.mark.parametrize("N,K", [(1, 128), (37, 384), (100, 1152), (16, 256), (33, 640), (129, 2048), (8, 128)])
+@pytest.mark.parametrize("M", [1, 3, 8, 9])
+def test_ragged_shapes(oracle_mod, N, K, M):
+    """Row tails (N % 16 != 0), odd block counts (K/128 odd, blocks at 2 mod 4
+    offsets, the last block ending mid-dword) and chunk boundaries."""
+    A, codes, d, packed = _case(11, N, K, M, salt=N * 7 + K)
+    Bd = dev_u8(packed)
+    got = q2_0_gpu(A, Bd, N, K, extra_rows=2)
+    assert np.all(got[M:] == CANARY)
+    got = got[:M]
+    check_parity(got, oracle_mod.q2_0_gemv(A, codes, d), f"q2_0 N={N} K={K} M={M}")
+    assert np.array_equal(got, _m1_rows(A, Bd, N, K))
+
+
+@pytest.mark.parametrize("N,K,M", [(64, 1024, 1), (37, 640, 8), (300, 5120, 16)])
+def test_exact_integer_regime_bit_identical(oracle_mod, N, K, M):
+    """a in [-8,8] integers, d = 2^-j: exact in fp32 in any order, so the GPU
+    must equal the oracle bit for bit."""
+    A = gen.exact_activations(N + M, M, K)
+    codes = gen.rng(902, 2, N).integers(0, 3, size=(N, K), dtype=np.uint8)
+    d = gen.exact_q2_0_scales(N * K, N, K)
+    got = q2_0_gpu(A, wqd.q2_0_pack(codes, d), N, K)
+    assert np.array_equal(got, oracle_mod.q2_0_gemv(A, codes, d))
+
+
+def test_code_3_decodes_to_plus_2d(oracle_mod):
+    """The layout admits code 3 (the packer rejects it); (code & 3) - 1 makes it +2d."""
+    N, K, M = 24, 512, 2
+    A = gen.activations(12, K, M)
+    codes = gen.rng(903, 2).integers(0, 3, size=(N, K), dtype=np.uint8)
+    d = gen.f16_bits(np.full((N, K // 128), 0.03))
+    packed = wqd.q2_0_pack(codes, d).copy()
+    r = gen.rng(903, 9)
+    for n in range(N):
+        for k in r.choice(K, 9, replace=False):
+            codes[n, k] = 3
+            blk = (n * (K // 128) + k // 128) * 34
+            packed[blk + 2 + (k % 128) // 4] |= np.uint8(3 << (2 * (k % 4)))
+    c2, _ = oracle_mod.q2_0_unpack(packed, N, K)
+    assert np.array_equal(c2, codes)
+    check_parity(q2_0_gpu(A, packed, N, K), oracle_mod.q2_0_gemv(A, codes, d), "code 3")
+
+
+def test_closed_forms_on_gpu(oracle_mod):
+    """All codes 1 gives +0; one nonzero code gives bf16(a_k * (c-1) * d)."""
+    N, K = 20, 1024
+    A = gen.activations(13, K, 3)
+    d = gen.f16_bits(np.abs(gen.rng(904, 3).normal(0, 0.02, (N, K // 128))) + 1e-3)
+    ones = np.ones((N, K), np.uint8)
+    got = q2_0_gpu(A, wqd.q2_0_pack(ones, d), N, K)
+    assert np.all(got == 0)
+    single = ones.copy()
+    ks = gen.rng(904, 4).integers(0, K, N)
+    single[np.arange(N), ks] = np.where(np.arange(N) % 2 == 0, 0, 2)
+    got = q2_0_gpu(A, wqd.q2_0_pack(single, d), N, K)
+    assert np.array_equal(got, oracle_mod.q2_0_gemv(A, single, d))
+
+
+def test_worked_examples_on_gpu():
+    """The closed-form examples of the golden file, bit for bit."""
+    exs = {e["name"]: int(e["expected_bf16"], 16) for e in json.load(open(GOLDEN))["examples"]}
+    from test_oracle_q2_0 import _example_inputs
+    for name, expected in exs.items():
+        K, A, codes, d = _example_inputs(name)
+        got = q2_0_gpu(A, wqd.q2_0_pack(codes, d), 1, K, single=True)
+        assert int(got[0, 0]) == expected, name
+
+
+@pytest.mark.parametrize("N,K", [(17408, 5120), (5120, 17408)])
+def test_ffn_shapes(oracle_mod, N, K):
+    """FFN up/down shapes: M=1 in full; M=8 and M=32 (four 8-row launches)
+    bit-identical to M=1 per row and within tolerance on a row sample."""
+    A, codes, d, packed = _case(5, N, K, 32)
+    Bd = dev_u8(packed)
+    got1 = q2_0_gpu(A[:1], Bd, N, K, single=True)
+    check_parity(got1, oracle_mod.q2_0_gemv(A[:1], codes, d), f"q2_0 {N}x{K} M=1")
+    got32 = q2_0_gpu(A, Bd, N, K)
+    got8 = q2_0_gpu(A[:8], Bd, N, K)
+    assert np.array_equal(got8, got32[:8])
+    for m in (0, 7, 8, 21, 31):
+        assert np.array_equal(got32[m:m + 1], q2_0_gpu(A[m:m + 1], Bd, N, K, single=True))
+    cols = np.sort(gen.rng(905, N, K).choice(N, 512, replace=False))
+    ref = oracle_mod.q2_0_gemv(A, codes[cols], d[cols])
+    check_parity(got32[:, cols], ref, f"q2_0 {N}x{K} M=32 sampled")

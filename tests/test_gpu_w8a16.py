@@ -1,0 +1,95 @@
+"""GPU parity of the W8A16 M16 GEMM against the CPU oracle, through the C ABI.
+
+Bar: every output within 2 BF16 ulp or 1e-2 x row RMS of the oracle; each
+output row bit-identical whatever M is; the exact-integer regime bit-identical
+to the oracle; rows >= M never written (page "w8a16_gemm_m16.rs", doc of
+w8a16_gemm_m16).
+"""
+import numpy as np
+import pytest
+import torch
+
+from parity import CANARY, check_parity, dev_f32, dev_u8, requires_gpu, ulp_histogram, w8a16_gpu
+from weight_quantized_decode_block_amd import inputs as gen
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+
+def _case(wid, N, K, M, salt=0):
+    A = gen.activations(wid, K, M, salt)
+    W, S = gen.w8a16_weights(wid, N, K, salt)
+    return A, W, S
+
+
+def test_all_256_e4m3fn_codes_decode_on_device(oracle_mod):
+    """W[n,0] = code n, A = e_0, S = 1: C[0,n] is the device's decode of code n."""
+    N, K = 256, 128
+    W = np.zeros((N, K), np.uint8)
+    W[:, 0] = np.arange(256, dtype=np.uint8)
+    A = np.zeros((1, K), np.float32)
+    A[0, 0] = 1.0
+    got = w8a16_gpu(gen.bf16_bits(A), W, np.ones((2, 1), np.float32), N, K)[0]
+    ref = torch.from_numpy(np.arange(256, dtype=np.uint8)).view(torch.float8_e4m3fn).float().numpy()
+    gv = gen.bf16_values(got)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(gv), nan)
+    assert np.array_equal(gv[~nan], ref[~nan])
+    assert np.array_equal(got[~nan], oracle_mod.w8a16_gemm(gen.bf16_bits(A), W, np.ones((2, 1), np.float32))[0][~nan])
+
+
+@pytest.mark.parametrize("M", [1, 8, 16])
+def test_qkv_parity(oracle_mod, M):
+    """N=K=5120, M in {1, 8, 16}."""
+    A, W, S = _case(4, 5120, 5120, M)
+    got = w8a16_gpu(A, W, S, 5120, 5120)
+    ref = oracle_mod.w8a16_gemm(A, W, S)
+    check_parity(got, ref, f"w8a16 5120^2 M={M}")
+    print("ulp histogram", ulp_histogram(got, ref))
+
+
+def test_rows_bit_identical_across_m(oracle_mod):
+    N, K = 5120, 5120
+    A, W, S = _case(4, N, K, 16)
+    Wd, Sd = dev_u8(W), dev_f32(S)
+    full = w8a16_gpu(A, Wd, Sd, N, K)
+    assert np.array_equal(w8a16_gpu(A[:8], Wd, Sd, N, K), full[:8])
+    for m in (0, 5, 15):
+        assert np.array_equal(w8a16_gpu(A[m:m + 1], Wd, Sd, N, K), full[m:m + 1])
+
+
+@pytest.mark.parametrize("N,K,M", [(130, 1024, 16), (16, 128, 1), (300, 640, 7)])
+def test_exact_integer_regime_bit_identical(oracle_mod, N, K, M):
+    A = gen.exact_activations(N + M + 1, M, K)
+    W, S = gen.exact_w8a16_weights(N * 3 + K, N, K)
+    got = w8a16_gpu(A, W, S, N, K)
+    assert np.array_equal(got, oracle_mod.w8a16_gemm(A, W, S))
+
+
+@pytest.mark.parametrize("N,K,M", [(17, 384, 3), (130, 1152, 16), (1, 128, 1), (200, 256, 9), (4095, 640, 2)])
+def test_ragged_shapes_and_canary_rows(oracle_mod, N, K, M):
+    A, W, S = _case(14, N, K, M, salt=N + K)
+    got = w8a16_gpu(A, W, S, N, K, c_rows=16)
+    assert np.all(got[M:] == CANARY)
+    check_parity(got[:M], oracle_mod.w8a16_gemm(A, W, S), f"w8a16 N={N} K={K} M={M}")
+
+
+@pytest.mark.parametrize("N,K", [(17408, 5120), (5120, 17408)])
+def test_ffn_shapes(oracle_mod, N, K):
+    """FFN up/down shapes: M=16 in full, M=1 bit-identical to row 0, and M=32
+    as two calls on contiguous 16-row halves (the page's row-halves rule)."""
+    A, W, S = _case(5, N, K, 32)
+    Wd, Sd = dev_u8(W), dev_f32(S)
+    got16 = w8a16_gpu(A[:16], Wd, Sd, N, K)
+    check_parity(got16, oracle_mod.w8a16_gemm(A[:16], W, S), f"w8a16 {N}x{K} M=16")
+    assert np.array_equal(w8a16_gpu(A[:1], Wd, Sd, N, K), got16[:1])
+    Ad = torch.from_numpy(A.view(np.int16)).to("cuda")
+    C = torch.full((32, N), CANARY, dtype=torch.int16, device="cuda")
+    from weight_quantized_decode_block_amd import wqd
+    wqd.w8a16_gemm_m16(Ad[:16], Wd, Sd, C[:16], 16, N, K)
+    wqd.w8a16_gemm_m16(Ad[16:], Wd, Sd, C[16:], 16, N, K)
+    torch.cuda.synchronize()
+    got32 = C.cpu().numpy().view(np.uint16)
+    assert np.array_equal(got32[:16], got16)
+    cols = np.sort(gen.rng(906, N, K).choice(N, 384, replace=False))
+    ref = np.concatenate([oracle_mod.w8a16_gemm(A[16:], W[c:c + 1], S[c // 128:c // 128 + 1]) for c in cols], axis=1)
+    check_parity(got32[16:, cols], ref, f"w8a16 {N}x{K} rows 16..31 sampled")

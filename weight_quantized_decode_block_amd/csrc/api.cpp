@@ -1,0 +1,151 @@
+// C-ABI layer of libwqd.so: argument validation, Q2_0 row chunking, device
+// checks and launch dispatch.  Every check runs before the first HIP call, so
+// argument errors are reported the same way on a machine without a GPU.
+//
+// Behaviour follows page "gemv_q2_vec.rs" (q2_0_gemv_vec launcher; the
+// batched launcher's Q2_BATCHM_MAX_M chunking, batchm_row_chunks and
+// batchm_launch_chunks) and page "w8a16_gemm_m16.rs" (w8a16_gemm_m16's checks
+// 1 <= m <= 16 and K % 128 == 0).
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/wqd.h"
+#include "wqd_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// 0 = not yet checked, 1 = gfx950, 2 = other architecture.
+constexpr int kMaxDevices = 64;
+int g_dev_state[kMaxDevices] = {0};
+std::mutex g_dev_mu;
+
+// Confirms a current HIP device exists and is a gfx950 part (the only code
+// object this library carries).
+int check_device(const char *fn) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0) {
+    int count = 0;
+    (void)hipGetDeviceCount(&count);
+    (void)hipGetLastError();
+    return fail(WQD_ENODEV, "%s: no usable HIP device (%s)", fn, hipGetErrorString(e));
+  }
+  if (dev >= kMaxDevices) return fail(WQD_ENODEV, "%s: device index %d too large", fn, dev);
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (g_dev_state[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(WQD_EHIP, "%s: hipGetDeviceProperties: %s", fn, hipGetErrorString(e));
+    g_dev_state[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+  }
+  if (g_dev_state[dev] != 1)
+    return fail(WQD_EUNSUPPORTED, "%s: device %d is not gfx950 (this library carries gfx950 code only)", fn, dev);
+  return WQD_OK;
+}
+
+int check_launch(const char *fn, hipError_t e) {
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) return fail(WQD_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return WQD_OK;
+}
+
+int validate_q2_0(const char *fn, const void *A, const void *B, void *C, uint32_t N,
+                  uint32_t K, uint32_t group) {
+  if (!A || !B || !C) return fail(WQD_ENULL, "%s: A, B and C must be non-NULL", fn);
+  if (group != WQD_Q2_0_GROUP) return fail(WQD_EINVAL, "%s: group=%u, only 128 is supported", fn, group);
+  if (N == 0) return fail(WQD_EINVAL, "%s: N must be >= 1", fn);
+  if (K == 0 || K % WQD_Q2_0_GROUP != 0) return fail(WQD_EINVAL, "%s: K=%u is not a positive multiple of 128", fn, K);
+  if (!aligned(A, 16)) return fail(WQD_EALIGN, "%s: A must be 16-byte aligned", fn);
+  if (!aligned(B, 4)) return fail(WQD_EALIGN, "%s: B must be 4-byte aligned", fn);
+  if (!aligned(C, 2)) return fail(WQD_EALIGN, "%s: C must be 2-byte aligned", fn);
+  return WQD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *wqd_last_error(void) { return g_last_error; }
+
+size_t q2_0_packed_bytes(uint32_t N, uint32_t K) {
+  if (K % WQD_Q2_0_GROUP != 0) return 0;
+  return static_cast<size_t>(N) * (K / WQD_Q2_0_GROUP) * WQD_Q2_0_BLOCK_BYTES;
+}
+
+uint32_t q2_0_batchm_chunks(uint32_t M, uint32_t K, uint32_t N, uint64_t *out3, uint32_t cap) {
+  uint32_t count = 0;
+  for (uint32_t r0 = 0; r0 < M; r0 += WQD_Q2_0_BATCHM_MAX_M, ++count) {
+    uint32_t rows = (M - r0) < WQD_Q2_0_BATCHM_MAX_M ? (M - r0) : WQD_Q2_0_BATCHM_MAX_M;
+    if (out3 && count < cap) {
+      out3[3 * count + 0] = static_cast<uint64_t>(r0) * K * 2;
+      out3[3 * count + 1] = static_cast<uint64_t>(r0) * N * 2;
+      out3[3 * count + 2] = rows;
+    }
+  }
+  return count;
+}
+
+int q2_0_gemv(const void *A, const void *B, void *C, uint32_t N, uint32_t K, uint32_t group,
+              hipStream_t stream) {
+  static const char fn[] = "q2_0_gemv";
+  int rc = validate_q2_0(fn, A, B, C, N, K, group);
+  if (rc) return rc;
+  if ((rc = check_device(fn))) return rc;
+  (void)hipGetLastError();
+  return check_launch(fn, wqd::launch_q2_0(A, B, C, N, K, 1, stream));
+}
+
+int q2_0_gemv_batchm(const void *A, const void *B, void *C, uint32_t N, uint32_t K,
+                     uint32_t group, uint32_t M, hipStream_t stream) {
+  static const char fn[] = "q2_0_gemv_batchm";
+  int rc = validate_q2_0(fn, A, B, C, N, K, group);
+  if (rc) return rc;
+  if (M == 0) return WQD_OK;  // no rows: nothing to launch
+  if ((rc = check_device(fn))) return rc;
+  (void)hipGetLastError();
+  const char *a = static_cast<const char *>(A);
+  char *c = static_cast<char *>(C);
+  for (uint32_t r0 = 0; r0 < M; r0 += WQD_Q2_0_BATCHM_MAX_M) {
+    uint32_t rows = (M - r0) < WQD_Q2_0_BATCHM_MAX_M ? (M - r0) : WQD_Q2_0_BATCHM_MAX_M;
+    rc = check_launch(fn, wqd::launch_q2_0(a + static_cast<size_t>(r0) * K * 2, B,
+                                           c + static_cast<size_t>(r0) * N * 2, N, K, rows, stream));
+    if (rc) return rc;
+  }
+  return WQD_OK;
+}
+
+int w8a16_gemm_m16(const void *A, const void *W, const float *S, void *C, uint32_t M, uint32_t N,
+                   uint32_t K, hipStream_t stream) {
+  static const char fn[] = "w8a16_gemm_m16";
+  if (!A || !W || !S || !C) return fail(WQD_ENULL, "%s: A, W, S and C must be non-NULL", fn);
+  if (M < 1 || M > WQD_W8A16_MAX_M) return fail(WQD_EINVAL, "%s: m=%u outside 1..16 (the M tile)", fn, M);
+  if (K == 0 || K % WQD_W8A16_BLOCK != 0)
+    return fail(WQD_EINVAL, "%s: K=%u is not a positive multiple of 128 (block-scale granularity)", fn, K);
+  if (N == 0) return fail(WQD_EINVAL, "%s: N must be >= 1", fn);
+  if (!aligned(A, 16)) return fail(WQD_EALIGN, "%s: A must be 16-byte aligned", fn);
+  if (!aligned(W, 16)) return fail(WQD_EALIGN, "%s: W must be 16-byte aligned", fn);
+  if (!aligned(S, 4)) return fail(WQD_EALIGN, "%s: S must be 4-byte aligned", fn);
+  if (!aligned(C, 2)) return fail(WQD_EALIGN, "%s: C must be 2-byte aligned", fn);
+  int rc = check_device(fn);
+  if (rc) return rc;
+  (void)hipGetLastError();
+  return check_launch(fn, wqd::launch_w8a16_m16(A, W, S, C, M, N, K, stream));
+}
+
+}  // extern "C"
