@@ -1,0 +1,353 @@
+#!/usr/bin/env python3
+"""Throughput of the weight-only-quantized decode GEMV on one MI355X.
+
+Headline workload: Q2_0 ternary GEMV, M=1, N=K=5120 (an attention qkv/o-sized
+projection), weights cold-cycled through a ring of distinct copies larger than
+the 256 MB Infinity Cache.  One step = one q2_0_gemv call on the next ring
+copy, with the activations and every weight copy already resident in HBM.
+
+Metric: effective weight-stream bandwidth = packed weight bytes per call
+(N*(K/128)*34) / time per call, and its fraction of the 8 TB/s HBM peak.
+
+Prints one JSON line (rank 0, N=1).  Extra keys: ``roofline`` (the kernel's
+own average duration from HIP events on its stream, against HBM peak),
+``cpu_baseline`` (the CPU oracle timed on host cores over a bounded sample)
+and ``sweep`` (the other synthetic workloads: Q2_0 batched M, W8A16, FFN
+shapes), unless ``--no-sweep``.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "effective weight-stream GB/s & % HBM peak, Q2_0/FP8 GEMV N=K=5120, M=1..16"
+RING_BYTES = 512 * 1024 * 1024
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=2000)
+    p.add_argument("--warmup", type=int, default=200)
+    p.add_argument("--no-sweep", action="store_true", help="headline workload only")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--only", default=None, help="run a single sweep entry by name (profiling)")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="also run a plain 256 MiB device copy (reference for counter scaling)")
+    return p.parse_args()
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def ring_size(nbytes: int) -> int:
+    if nbytes < (1 << 20):  # the small correctness workload is latency-bound; no cold ring
+        return 8
+    return max(8, math.ceil(RING_BYTES / nbytes))
+
+
+def q2_0_bytes(N, K):
+    return N * (K // 128) * 34
+
+
+def fp8_bytes(N, K):
+    return N * K + ((N + 127) // 128) * (K // 128) * 4
+
+
+# ------------------------------------------------------------------ workloads
+class Q2Workload:
+    fmt = "q2_0"
+
+    def __init__(self, name, wid, N, K, M):
+        self.name, self.wid, self.N, self.K, self.M = name, wid, N, K, M
+        self.bytes = q2_0_bytes(N, K)
+
+    def setup(self, torch, gen, wqd):
+        N, K, M = self.N, self.K, self.M
+        A = gen.activations(self.wid, K, M)
+        codes, d = gen.q2_0_weights(self.wid, N, K)
+        packed = wqd.q2_0_pack(codes, d)
+        self.host = (A, codes, d)
+        row = (K // 128) * 34
+        base = torch.from_numpy(packed).to("cuda").view(N, row)
+        self.R = ring_size(self.bytes)
+        # copy i = copy 0 with its weight rows rotated by i (distinct bytes and addresses)
+        self.ring = [torch.roll(base, shifts=i, dims=0).contiguous().view(-1) for i in range(self.R)]
+        del base
+        self.A = torch.from_numpy(A.view("int16")).to("cuda")
+        self.C = torch.empty((M, N), dtype=torch.int16, device="cuda")
+
+    def call(self, wqd, i):
+        B = self.ring[i % self.R]
+        if self.M == 1:
+            wqd.q2_0_gemv(self.A, B, self.C, self.N, self.K)
+        else:
+            wqd.q2_0_gemv_batchm(self.A, B, self.C, self.N, self.K, 128, self.M)
+
+    def check(self, torch, np, oracle, check_fn, copy_idx):
+        A, codes, d = self.host
+        self.call(self._wqd, copy_idx)
+        torch.cuda.synchronize()
+        got = self.C.cpu().numpy().view(np.uint16)
+        cols = np.arange(self.N) if self.N * self.M <= 5120 * 16 else \
+            np.sort(np.random.Generator(np.random.PCG64(copy_idx)).choice(self.N, 1024, replace=False))
+        src = (cols - copy_idx) % self.N  # rolled rows
+        ref = oracle.q2_0_gemv(A, codes[src], d[src])
+        check_fn(got[:, cols], ref)
+
+    def oracle_call(self, oracle, nthreads):
+        A, codes, d = self.host
+        oracle.q2_0_gemv(A, codes, d, nthreads=nthreads)
+
+    def free(self):
+        self.ring = self.A = self.C = None
+
+
+class Fp8Workload:
+    fmt = "w8a16"
+
+    def __init__(self, name, wid, N, K, M):
+        self.name, self.wid, self.N, self.K, self.M = name, wid, N, K, M
+        self.bytes = fp8_bytes(N, K)
+
+    def setup(self, torch, gen, wqd):
+        N, K, M = self.N, self.K, self.M
+        A = gen.activations(self.wid, K, M)
+        W, S = gen.w8a16_weights(self.wid, N, K)
+        self.host = (A, W, S)
+        base = torch.from_numpy(W).to("cuda")
+        self.R = ring_size(self.bytes)
+        self.ring = [torch.roll(base, shifts=i, dims=0).contiguous() for i in range(self.R)]
+        del base
+        self.S = torch.from_numpy(S).to("cuda")
+        self.A = torch.from_numpy(A.view("int16")).to("cuda")
+        self.C = torch.empty((M, N), dtype=torch.int16, device="cuda")
+
+    def call(self, wqd, i):
+        W = self.ring[i % self.R]
+        for r0 in range(0, self.M, 16):  # 17..32 rows: two calls on contiguous halves
+            rows = min(16, self.M - r0)
+            wqd.w8a16_gemm_m16(self.A[r0:r0 + rows], W, self.S, self.C[r0:r0 + rows], rows, self.N, self.K)
+
+    def check(self, torch, np, oracle, check_fn, copy_idx):
+        A, W, S = self.host
+        self.call(self._wqd, copy_idx)
+        torch.cuda.synchronize()
+        got = self.C.cpu().numpy().view(np.uint16)
+        cols = np.sort(np.random.Generator(np.random.PCG64(copy_idx)).choice(self.N, 256, replace=False))
+        src = (cols - copy_idx) % self.N
+        ref = np.concatenate([oracle.w8a16_gemm(A, W[s:s + 1], S[c // 128:c // 128 + 1])
+                              for s, c in zip(src, cols)], axis=1)
+        check_fn(got[:, cols], ref)
+
+    def oracle_call(self, oracle, nthreads):
+        A, W, S = self.host
+        oracle.w8a16_gemm(A, W, S, nthreads=nthreads)
+
+    def free(self):
+        self.ring = self.A = self.C = self.S = None
+
+
+HEADLINE = ("q2_0 M=1 N=5120 K=5120", Q2Workload, 2, 5120, 5120, 1)
+
+
+def sweep_list():
+    out = [("q2_0 M=1 N=256 K=1024", Q2Workload, 1, 256, 1024, 1)]
+    for M in (2, 4, 5, 8, 16):
+        out.append((f"q2_0 M={M} N=5120 K=5120", Q2Workload, 3, 5120, 5120, M))
+    for M in (1, 8, 16):
+        out.append((f"w8a16 M={M} N=5120 K=5120", Fp8Workload, 4, 5120, 5120, M))
+    for (N, K) in ((17408, 5120), (5120, 17408)):
+        for M in (1, 8, 16, 32):
+            out.append((f"q2_0 M={M} N={N} K={K}", Q2Workload, 5, N, K, M))
+            out.append((f"w8a16 M={M} N={N} K={K}", Fp8Workload, 5, N, K, M))
+    return out
+
+
+# ------------------------------------------------------------------- timing
+def time_workload(torch, wqd, wl, steps, warmup):
+    """Whole-region time per step (events around the loop) and the average
+    duration of one step's launches (events bracketing each step, a second
+    pass), both on the stream the kernels run on."""
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        wl.call(wqd, i)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(steps):
+        wl.call(wqd, warmup + i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+
+    n_kernel = min(steps, 500)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_kernel)]
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        wl.call(wqd, warmup + steps + i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in evs)
+    kern_ms = sum(per) / len(per)
+    return total_ms / steps, kern_ms, per[len(per) // 2]
+
+
+def cpu_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except Exception:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def traffic_from_profile(kernel_src: str, name: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source (else None)."""
+    prof = os.path.join(ROOT, "profiles", f"{name}.md")
+    if not os.path.exists(prof):
+        return None
+    text = open(prof).read()
+    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m_t = re.search(r"traffic_bytes_per_launch:\s*([0-9.]+)", text)
+    if not m_sha or not m_t or m_sha.group(1) != sha:
+        return None
+    return float(m_t.group(1))
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the kernels would shard by output rows; see the design notes). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from weight_quantized_decode_block_amd import inputs as gen
+    from weight_quantized_decode_block_amd import wqd
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    wqd.lib()
+
+    import oracle  # parity checks and the CPU baseline only
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from parity import check_parity
+
+    def run(entry, steps, warmup):
+        name, cls, wid, N, K, M = entry
+        wl = cls(name, wid, N, K, M)
+        wl._wqd = wqd
+        t = time.time()
+        wl.setup(torch, gen, wqd)
+        log(f"[bench] {name}: ring of {wl.R} copies x {wl.bytes} B set up in {time.time() - t:.1f}s")
+        wl.check(torch, np, oracle, lambda g, r: check_parity(g, r, name), 0)
+        wl.check(torch, np, oracle, lambda g, r: check_parity(g, r, name), wl.R // 2 + 1)
+        step_ms, kern_ms, kern_med = time_workload(torch, wqd, wl, steps, warmup)
+        res = {"workload": name, "format": wl.fmt, "N": N, "K": K, "M": M, "ring": wl.R,
+               "bytes_per_call": wl.bytes, "us_per_call": round(step_ms * 1e3, 3),
+               "kernel_us_avg": round(kern_ms * 1e3, 3), "kernel_us_median": round(kern_med * 1e3, 3),
+               "gbs": round(wl.bytes / (step_ms * 1e-3) / 1e9, 1),
+               "kernel_gbs": round(wl.bytes / (kern_ms * 1e-3) / 1e9, 1)}
+        res["frac_hbm"] = round(res["gbs"] / HBM_PEAK_GBS, 4)
+        res["kernel_frac_hbm"] = round(res["kernel_gbs"] / HBM_PEAK_GBS, 4)
+        log(f"[bench] {name}: {res['us_per_call']} us/call, {res['gbs']} GB/s "
+            f"(kernel {res['kernel_us_avg']} us, {res['kernel_gbs']} GB/s)")
+        return wl, res
+
+    if args.only:
+        entries = [e for e in [HEADLINE] + sweep_list() if e[0] == args.only]
+        if not entries:
+            sys.exit(f"unknown workload {args.only!r}")
+        wl, res = run(entries[0], args.steps, args.warmup)
+        print(json.dumps({"only": res}))
+        return
+
+    if args.copy_probe:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy probe: 5 copies of 268435456 B done")
+        del src, dst
+
+    wl, head = run(HEADLINE, args.steps, args.warmup)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        nthr = cpu_threads()
+        calls, t0 = 0, time.perf_counter()
+        while True:
+            wl.oracle_call(oracle, nthr)
+            calls += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+        cpu = {"value": round(wl.bytes * calls / el / 1e9, 4), "unit": "GB/s", "cores": nthr,
+               "kind": "oracle",
+               "sample": f"oracle_q2_0_gemv over the whole N=K=5120 M=1 workload (ring copy 0), "
+                         f"{calls} calls in {el:.2f} s on {nthr} threads"}
+        log(f"[bench] cpu oracle: {cpu['value']} GB/s ({calls} calls, {el:.1f}s, {nthr} threads)")
+    wl.free()
+    torch.cuda.empty_cache()
+
+    sweep = []
+    if not args.no_sweep:
+        for entry in sweep_list():
+            w2, r2 = run(entry, min(args.steps, 1000), min(args.warmup, 100))
+            w2.free()
+            torch.cuda.empty_cache()
+            sweep.append(r2)
+
+    kern_src = os.path.join(ROOT, "weight_quantized_decode_block_amd", "csrc", "q2_0_gemv.hip")
+    achieved = head["kernel_gbs"]
+    line = {
+        "metric": METRIC,
+        "value": head["gbs"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["us_per_call"] / 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "Q2_0 ternary GEMV M=1 N=5120 K=5120 group=128, bf16 activations, "
+                               f"weights cold-cycled through {head['ring']} distinct copies "
+                               f"({head['ring'] * head['bytes_per_call'] / 2**20:.0f} MiB)",
+                   "bytes_per_call": head["bytes_per_call"], "frac_hbm_peak": head["frac_hbm"],
+                   "us_per_call": head["us_per_call"]},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from_profile(kern_src, "q2_0_gemv_kernel_m1_5120x5120"),
+                     "kernel": "q2_0_gemv_kernel<1>", "kernel_us_avg": head["kernel_us_avg"]},
+        "cpu_baseline": cpu,
+    }
+    if sweep:
+        line["sweep"] = sweep
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -10,6 +10,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -57,6 +58,23 @@ int check_device(const char *fn) {
   if (g_dev_state[dev] != 1)
     return fail(WQD_EUNSUPPORTED, "%s: device %d is not gfx950 (this library carries gfx950 code only)", fn, dev);
   return WQD_OK;
+}
+
+// Kernel choice for Q2_0.  The matrix-core kernel serves every K that is a
+// multiple of 1024; other K use the vector-ALU kernel.  The presence of
+// WQD_Q2_0_VALU (any value; read once per process) forces the vector-ALU
+// kernel everywhere, for A/B runs.  The choice depends only on K, never on M,
+// so batched rows stay bit-identical to M=1 rows; the two kernels differ from
+// each other only by fp32 rounding order.
+bool q2_0_use_valu(uint32_t K, uint32_t m) {
+  static const bool forced = std::getenv("WQD_Q2_0_VALU") != nullptr;
+  return forced || !wqd::q2_0_mfma_supports(K, m);
+}
+
+hipError_t launch_q2_0(const void *A, const void *B, void *C, uint32_t N, uint32_t K, uint32_t m,
+                       hipStream_t stream) {
+  return q2_0_use_valu(K, m) ? wqd::launch_q2_0_valu(A, B, C, N, K, m, stream)
+                             : wqd::launch_q2_0_mfma(A, B, C, N, K, m, stream);
 }
 
 int check_launch(const char *fn, hipError_t e) {
@@ -108,7 +126,7 @@ int q2_0_gemv(const void *A, const void *B, void *C, uint32_t N, uint32_t K, uin
   if (rc) return rc;
   if ((rc = check_device(fn))) return rc;
   (void)hipGetLastError();
-  return check_launch(fn, wqd::launch_q2_0(A, B, C, N, K, 1, stream));
+  return check_launch(fn, launch_q2_0(A, B, C, N, K, 1, stream));
 }
 
 int q2_0_gemv_batchm(const void *A, const void *B, void *C, uint32_t N, uint32_t K,
@@ -123,7 +141,7 @@ int q2_0_gemv_batchm(const void *A, const void *B, void *C, uint32_t N, uint32_t
   char *c = static_cast<char *>(C);
   for (uint32_t r0 = 0; r0 < M; r0 += WQD_Q2_0_BATCHM_MAX_M) {
     uint32_t rows = (M - r0) < WQD_Q2_0_BATCHM_MAX_M ? (M - r0) : WQD_Q2_0_BATCHM_MAX_M;
-    rc = check_launch(fn, wqd::launch_q2_0(a + static_cast<size_t>(r0) * K * 2, B,
+    rc = check_launch(fn, launch_q2_0(a + static_cast<size_t>(r0) * K * 2, B,
                                            c + static_cast<size_t>(r0) * N * 2, N, K, rows, stream));
     if (rc) return rc;
   }

@@ -265,7 +265,7 @@ hipError_t launch_mc(const void *A, const void *B, void *C, uint32_t N, uint32_t
 
 }  // namespace
 
-hipError_t launch_q2_0(const void *A, const void *B, void *C, uint32_t N, uint32_t K, uint32_t m,
+hipError_t launch_q2_0_valu(const void *A, const void *B, void *C, uint32_t N, uint32_t K, uint32_t m,
                        hipStream_t stream) {
   switch (m) {
     case 1: return launch_mc<1>(A, B, C, N, K, stream);
