@@ -67,15 +67,17 @@ constexpr int kAPhaseBytes = kPhaseBlocks * 256;          // 4096 bytes of one a
 constexpr int kAPitch = kAPhaseBytes + 16;                // LDS pitch of an activation row
 constexpr int kSecond = 8;                                // a wave's second block of a phase: w + 8
 
-// LDS: [buffer 0][buffer 1][zero rows: kAPhaseBytes][dummy: 16 bytes]; a
-// buffer holds 16 weight-row segments and MMAX activation-row segments.
+// LDS: [buffer 0][buffer 1][zero rows: kAPhaseBytes][dummy: 16 bytes]
+// [partial tiles: kWaves x 16 x 16 floats]; a buffer holds 16 weight-row
+// segments and MMAX activation-row segments.
 template <int MMAX>
 struct Layout {
   static constexpr int kSlots = 2 + (MMAX * (kAPhaseBytes / 16) + kThreads - 1) / kThreads;
   static constexpr int kBuf = kWBytes + MMAX * kAPitch;
   static constexpr int kZero = 2 * kBuf;
   static constexpr int kDummy = kZero + kAPhaseBytes;
-  static constexpr int kTotal = kDummy + 16;
+  static constexpr int kPart = kDummy + 16;
+  static constexpr int kTotal = kPart + kWaves * 256 * 4;
 };
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
@@ -107,63 +109,60 @@ __device__ __forceinline__ void decode_word(uint32_t w, bf16x8_t &lo, bf16x8_t &
   hi = __builtin_bit_cast(bf16x8_t, b);
 }
 
-// One 16-byte chunk slot of a thread, fixed for the whole kernel.  Slots 0-1
-// carry weight chunks: row r = tid/32, column col = tid%32 + 32s of the row's
-// phase segment.  Slots 2.. carry activation chunks: c = (s-2)*512 + tid,
-// row m = c/256, column c%256.  `off` is the byte offset from the phase's
-// scalar base (the row is clamped to 0 when it does not exist), `lds` the
-// destination inside a buffer, `live` whether the row exists.
-struct Slot {
-  uint32_t off, lds, col;
-  bool live;
+// The 16-byte chunk slots of a thread, fixed for the whole kernel.  Slots 0-1
+// carry weight chunks: row r = tid/32 of the tile, column col = tid%32 + 32s
+// of the row's phase segment (34 columns).  Slots 2.. carry activation chunks:
+// c = (s-2)*512 + tid, row m = c/256, column c%256 (256 columns).  A weight
+// row past N re-reads row N-1 (its columns are never stored); an activation
+// row past M, or any column past the phase's end, re-reads an in-bounds chunk
+// and is stored to the dummy LDS slot.
+struct Chunks {
+  const uint8_t *B, *A;
+  uint32_t N, K, M, rb;
 };
 
 template <int S>
-__device__ __forceinline__ void make_slots(Slot (&sl)[S], uint32_t tid, uint32_t N, uint32_t n0, uint32_t rb,
-                                           uint32_t K, uint32_t M) {
+__device__ __forceinline__ void issue_phase(const Chunks &ck, uint32_t tid, uint32_t n0, uint32_t p, uint32_t pbn,
+                                            u32x4_t (&r)[S]) {
+  const uint32_t wcols = pbn * kBlockBytes / 16u, acols = pbn * 16u;
+  const uint32_t wph = pbn ? p * kPhaseWBytes : 0u, aph = pbn ? p * kAPhaseBytes : 0u;
 #pragma unroll
   for (int s = 0; s < S; ++s) {
+    uint32_t off;
+    const uint8_t *base;
     if (s < 2) {
-      const uint32_t r = tid >> 5, col = (tid & 31u) + 32u * s;
-      sl[s].live = n0 + r < N;
-      sl[s].off = (sl[s].live ? r : 0u) * rb + 16u * col;
-      sl[s].lds = r * kWPitch + 16u * col;
-      sl[s].col = col;
+      const uint32_t row = min(n0 + (tid >> 5), ck.N - 1u), col = (tid & 31u) + 32u * s;
+      off = row * ck.rb + wph + (col < wcols ? 16u * col : 0u);
+      base = ck.B;
     } else {
       const uint32_t c = (uint32_t)(s - 2) * kThreads + tid;
       const uint32_t m = c >> 8, col = c & 255u;
-      sl[s].live = m < M;
-      sl[s].off = (sl[s].live ? m : 0u) * K * 2u + 16u * col;
-      sl[s].lds = kWBytes + m * kAPitch + 16u * col;
-      sl[s].col = col;
+      off = (m < ck.M ? m : 0u) * ck.K * 2u + aph + (col < acols ? 16u * col : 0u);
+      base = ck.A;
     }
-  }
-}
-
-// Issue the loads of phase p, which has pbn blocks (0 when p is past the end;
-// then every slot re-reads phase 0's first column, which is in bounds).
-template <int S>
-__device__ __forceinline__ void issue_phase(const Slot (&sl)[S], const uint8_t *wbase, const uint8_t *abase,
-                                            uint32_t p, uint32_t pbn, u32x4_t (&r)[S]) {
-  const uint8_t *wb = pbn ? wbase + (size_t)p * kPhaseWBytes : wbase;
-  const uint8_t *ab = pbn ? abase + (size_t)p * kAPhaseBytes : abase;
-  const uint32_t wcols = pbn * kBlockBytes / 16u, acols = pbn * 16u;
-#pragma unroll
-  for (int s = 0; s < S; ++s) {
-    const bool in = sl[s].col < (s < 2 ? wcols : acols);
-    const uint32_t off = in ? sl[s].off : sl[s].off - 16u * sl[s].col;  // column 0 of the same row
-    r[s] = *reinterpret_cast<const u32x4_t *>((s < 2 ? wb : ab) + off);
+    r[s] = *reinterpret_cast<const u32x4_t *>(base + off);
   }
 }
 
 template <int S>
-__device__ __forceinline__ void write_phase(const Slot (&sl)[S], uint8_t *buf, uint8_t *dummy, uint32_t pbn,
-                                            const u32x4_t (&r)[S]) {
+__device__ __forceinline__ void write_phase(const Chunks &ck, uint32_t tid, uint8_t *buf, uint8_t *dummy,
+                                            uint32_t pbn, const u32x4_t (&r)[S]) {
   const uint32_t wcols = pbn * kBlockBytes / 16u, acols = pbn * 16u;
 #pragma unroll
   for (int s = 0; s < S; ++s) {
-    const bool ok = sl[s].live && sl[s].col < (s < 2 ? wcols : acols);
-    *reinterpret_cast<u32x4_t *>(ok ? buf + sl[s].lds : dummy) = r[s];
+    bool ok;
+    uint32_t lds_off;
+    if (s < 2) {
+      const uint32_t row = tid >> 5, col = (tid & 31u) + 32u * s;
+      ok = col < wcols;
+      lds_off = row * kWPitch + 16u * col;
+    } else {
+      const uint32_t c = (uint32_t)(s - 2) * kThreads + tid;
+      const uint32_t m = c >> 8, col = c & 255u;
+      ok = m < ck.M && col < acols;
+      lds_off = kWBytes + m * kAPitch + 16u * col;
+    }
+    *reinterpret_cast<u32x4_t *>(ok ? buf + lds_off : dummy) = r[s];
   }
 }
 
@@ -211,9 +210,14 @@ __global__ __launch_bounds__(kThreads) void q2_0_mfma_kernel(const uint16_t *__r
   const uint32_t i = lane & 15u, g = lane >> 4;
   const uint32_t nb = K >> 7;
   const uint32_t nphase = (nb + kPhaseBlocks - 1) / kPhaseBlocks;
-  const uint32_t n0 = blockIdx.x * 16u;
   const uint32_t rb = nb * kBlockBytes;
-  const uint8_t *wbase = B + (size_t)n0 * rb;
+  const uint32_t ntiles = (N + 15u) / 16u;
+  // This workgroup's tiles are blockIdx.x, blockIdx.x + gridDim.x, ...; its
+  // phases form one sequence q = j * nphase + p over them, and the load ring
+  // runs across tile boundaries so the next tile's first phases are already
+  // in flight when a tile ends.
+  const uint32_t my_tiles = (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x;
+  const uint32_t nq = my_tiles * nphase;
   const uint8_t *abase = reinterpret_cast<const uint8_t *>(A);
   uint8_t *dummy = lds + L::kDummy;
 
@@ -224,8 +228,15 @@ __global__ __launch_bounds__(kThreads) void q2_0_mfma_kernel(const uint16_t *__r
     *reinterpret_cast<u32x4_t *>(lds + L::kZero + 16u * tid) = z;
   }
 
-  Slot sl[L::kSlots];
-  make_slots<L::kSlots>(sl, tid, N, n0, rb, K, M);
+  const Chunks ck{B, abase, N, K, M, rb};
+  auto tile_of = [&](uint32_t j) { return blockIdx.x + j * gridDim.x; };
+  auto phase_blocks = [&](uint32_t p) { return min((uint32_t)kPhaseBlocks, nb - p * kPhaseBlocks); };
+  // Issue sequence element q (past the end: safe re-reads, stored nowhere).
+  auto issue_q = [&](uint32_t q, u32x4_t(&r)[L::kSlots]) {
+    const bool live = q < nq;
+    const uint32_t j = live ? q / nphase : 0u, p = live ? q - j * nphase : 0u;
+    issue_phase<L::kSlots>(ck, tid, tile_of(j) * 16u, p, live ? phase_blocks(p) : 0u, r);
+  };
 
   // This lane's read offsets (from the LDS base) for the wave's first block of
   // a phase in buffer 0; buffer 1 adds kBuf, the second block (w + 8) adds
@@ -237,61 +248,73 @@ __global__ __launch_bounds__(kThreads) void q2_0_mfma_kernel(const uint16_t *__r
   const uint32_t act = a_ok ? kWBytes + i * kAPitch + wave * 256u + 64u * g : L::kZero + 64u * g;
   const uint32_t act_buf = a_ok ? (uint32_t)L::kBuf : 0u;  // the zero region is shared by both buffers
   const uint32_t act_second = a_ok ? kSecond * 256u : 0u;
+  float *part = reinterpret_cast<float *>(lds + L::kPart);  // [wave][m][n]
 
   f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  auto blocks_in = [&](uint32_t q) { return q < nphase ? min((uint32_t)kPhaseBlocks, nb - q * kPhaseBlocks) : 0u; };
-  // One phase: store its chunks, request phase p+2 into the same registers,
-  // then compute on it.
-  auto step = [&](uint32_t p, uint32_t parity, u32x4_t(&r)[L::kSlots]) {
+  // Sequence element q: store its chunks (slots of its own tile), request
+  // element q+2 into the same registers, compute on it, and finish the tile
+  // after its last phase.
+  auto step = [&](uint32_t q, uint32_t parity, u32x4_t(&r)[L::kSlots]) {
+    const uint32_t j = q / nphase, p = q - j * nphase;
     uint8_t *buf = lds + parity * L::kBuf;
-    const uint32_t pbn = blocks_in(p);
-    write_phase<L::kSlots>(sl, buf, dummy, pbn, r);
-    issue_phase<L::kSlots>(sl, wbase, abase, p + 2u, blocks_in(p + 2u), r);
+    const uint32_t pbn = phase_blocks(p);
+    write_phase<L::kSlots>(ck, tid, buf, dummy, pbn, r);
+    issue_q(q + 2u, r);
     __syncthreads();
     const uint8_t *a0 = lds + act + parity * act_buf;
     if (wave < pbn) mac_block(buf + blk, buf + win, a0, sel, acc);
     if (wave + kSecond < pbn)
       mac_block(buf + blk + kSecond * kBlockBytes, buf + win + kSecond * kBlockBytes, a0 + act_second, sel, acc);
+    if (p + 1u == nphase) {  // tile done: add the 8 waves' partial tiles in fixed order
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) part[(wave * 16u + 4u * g + rr) * 16u + i] = acc[rr];
+      acc = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
+      __syncthreads();
+      if (tid < 256u) {
+        const uint32_t m = tid >> 4, col = tid & 15u;
+        const uint32_t n = tile_of(j) * 16u + col;
+        if (m < M && n < N) {
+          float v = part[m * 16u + col];
+          for (uint32_t w = 1; w < kWaves; ++w) v = v + part[(w * 16u + m) * 16u + col];
+          C[(size_t)m * N + n] = f32_to_bf16_rne(v);
+        }
+      }
+      // the next write of `part` comes after at least one more phase barrier
+    }
   };
 
   u32x4_t ring0[L::kSlots], ring1[L::kSlots];
-  issue_phase<L::kSlots>(sl, wbase, abase, 0u, blocks_in(0u), ring0);
-  issue_phase<L::kSlots>(sl, wbase, abase, 1u, blocks_in(1u), ring1);
-  uint32_t p = 0;
-  for (; p + 2u <= nphase; p += 2u) {
-    step(p, 0u, ring0);
-    step(p + 1u, 1u, ring1);
+  issue_q(0u, ring0);
+  issue_q(1u, ring1);
+  uint32_t q = 0;
+  for (; q + 2u <= nq; q += 2u) {
+    step(q, 0u, ring0);
+    step(q + 1u, 1u, ring1);
   }
-  if (p < nphase) step(p, 0u, ring0);
-
-  // Accumulator layout: this lane holds rows m = 4g + r of weight row n0 + i.
-  __syncthreads();  // every wave is done with the buffers
-  float *part = reinterpret_cast<float *>(lds);  // [wave][m][n]
-#pragma unroll
-  for (int r = 0; r < 4; ++r) part[(wave * 16u + 4u * g + r) * 16u + i] = acc[r];
-  __syncthreads();
-  if (tid < 256u) {
-    const uint32_t m = tid >> 4, col = tid & 15u;
-    const uint32_t n = n0 + col;
-    if (m < M && n < N) {
-      float v = part[m * 16u + col];
-      for (uint32_t w = 1; w < kWaves; ++w) v = v + part[(w * 16u + m) * 16u + col];
-      C[(size_t)m * N + n] = f32_to_bf16_rne(v);
-    }
-  }
+  if (q < nq) step(q, 0u, ring0);
 }
 
 template <int MMAX>
 hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32_t K, uint32_t M,
                        hipStream_t stream) {
-  static bool attr_set = false;  // one-time opt-in above the default LDS limit
-  if (!attr_set) {
+  // Persistent grid: as many workgroups as fit on the device at once, each
+  // walking every gridDim.x-th tile.  Resolved once per process.
+  static int resident = 0;
+  if (resident == 0) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&q2_0_mfma_kernel<MMAX>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, Layout<MMAX>::kTotal);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    int dev = 0, cus = 0, per_cu = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, q2_0_mfma_kernel<MMAX>, kThreads,
+                                                          Layout<MMAX>::kTotal)) != hipSuccess)
+      return e;
+    resident = (per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
   }
-  hipLaunchKernelGGL(q2_0_mfma_kernel<MMAX>, dim3((N + 15) / 16), dim3(kThreads), Layout<MMAX>::kTotal, stream,
+  const uint32_t ntiles = (N + 15) / 16;
+  const uint32_t grid = ntiles < (uint32_t)resident ? ntiles : (uint32_t)resident;
+  hipLaunchKernelGGL(q2_0_mfma_kernel<MMAX>, dim3(grid), dim3(kThreads), Layout<MMAX>::kTotal, stream,
                      static_cast<const uint16_t *>(A), static_cast<const uint8_t *>(B),
                      static_cast<uint16_t *>(C), N, K, M);
   return hipGetLastError();
