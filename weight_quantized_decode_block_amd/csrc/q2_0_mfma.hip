@@ -67,16 +67,16 @@ constexpr int kAPhaseBytes = kPhaseBlocks * 256;          // 4096 bytes of one a
 constexpr int kAPitch = kAPhaseBytes + 16;                // LDS pitch of an activation row
 constexpr int kSecond = 8;                                // a wave's second block of a phase: w + 8
 
-// LDS: [buffer 0][buffer 1][zero rows: kAPhaseBytes][dummy: 16 bytes]
-// [partial tiles: kWaves x 16 x 16 floats]; a buffer holds 16 weight-row
-// segments and MMAX activation-row segments.
+// LDS: [buffer 0][buffer 1][zero rows: kAPhaseBytes][partial tiles: kWaves x
+// 16 x 16 floats]; a buffer holds 16 weight-row segments, MMAX activation-row
+// segments and a 16-byte dummy slot at kDummy (buffer-relative).
 template <int MMAX>
 struct Layout {
   static constexpr int kSlots = 2 + (MMAX * (kAPhaseBytes / 16) + kThreads - 1) / kThreads;
-  static constexpr int kBuf = kWBytes + MMAX * kAPitch;
+  static constexpr int kDummy = kWBytes + MMAX * kAPitch;
+  static constexpr int kBuf = kDummy + 16;
   static constexpr int kZero = 2 * kBuf;
-  static constexpr int kDummy = kZero + kAPhaseBytes;
-  static constexpr int kPart = kDummy + 16;
+  static constexpr int kPart = kZero + kAPhaseBytes;
   static constexpr int kTotal = kPart + kWaves * 256 * 4;
 };
 
@@ -109,60 +109,47 @@ __device__ __forceinline__ void decode_word(uint32_t w, bf16x8_t &lo, bf16x8_t &
   hi = __builtin_bit_cast(bf16x8_t, b);
 }
 
-// The 16-byte chunk slots of a thread, fixed for the whole kernel.  Slots 0-1
-// carry weight chunks: row r = tid/32 of the tile, column col = tid%32 + 32s
-// of the row's phase segment (34 columns).  Slots 2.. carry activation chunks:
-// c = (s-2)*512 + tid, row m = c/256, column c%256 (256 columns).  A weight
-// row past N re-reads row N-1 (its columns are never stored); an activation
-// row past M, or any column past the phase's end, re-reads an in-bounds chunk
-// and is stored to the dummy LDS slot.
-struct Chunks {
-  const uint8_t *B, *A;
-  uint32_t N, K, M, rb;
+// The 16-byte chunk slots of a thread.  Slots 0-1 carry weight chunks: row
+// r = tid/32 of the tile, column col = tid%32 + 32s of the row's phase segment
+// (34 columns in a full phase).  Slots 2.. carry activation chunks: c =
+// (s-2)*512 + tid, row m = c/256, column c%256 (256 columns in a full phase).
+// Every slot keeps two precomputed (source offset, LDS destination) pairs: one
+// for full phases and one for the K tail's shorter phase.  A column past a
+// phase's end re-reads an in-bounds column and goes to the dummy LDS slot; an
+// activation row past M likewise.  A tile always has 16 real rows when N >= 16
+// (the last tile is shifted back to start at N - 16); for N < 16 a row past N
+// re-reads row N - 1 and its columns are never stored.  Source offsets are
+// relative to a per-phase scalar base, so issuing a phase costs one select per
+// slot.
+template <int S>
+struct Slots {
+  uint32_t src[2][S];  // [full, tail]
+  uint32_t dst[2][S];
 };
 
 template <int S>
-__device__ __forceinline__ void issue_phase(const Chunks &ck, uint32_t tid, uint32_t n0, uint32_t p, uint32_t pbn,
-                                            u32x4_t (&r)[S]) {
-  const uint32_t wcols = pbn * kBlockBytes / 16u, acols = pbn * 16u;
-  const uint32_t wph = pbn ? p * kPhaseWBytes : 0u, aph = pbn ? p * kAPhaseBytes : 0u;
+__device__ __forceinline__ void make_slots(Slots<S> &sl, uint32_t tid, uint32_t N, uint32_t rb, uint32_t K,
+                                           uint32_t M, uint32_t tail_blocks, uint32_t dummy) {
 #pragma unroll
-  for (int s = 0; s < S; ++s) {
-    uint32_t off;
-    const uint8_t *base;
-    if (s < 2) {
-      const uint32_t row = min(n0 + (tid >> 5), ck.N - 1u), col = (tid & 31u) + 32u * s;
-      off = row * ck.rb + wph + (col < wcols ? 16u * col : 0u);
-      base = ck.B;
-    } else {
-      const uint32_t c = (uint32_t)(s - 2) * kThreads + tid;
-      const uint32_t m = c >> 8, col = c & 255u;
-      off = (m < ck.M ? m : 0u) * ck.K * 2u + aph + (col < acols ? 16u * col : 0u);
-      base = ck.A;
-    }
-    r[s] = *reinterpret_cast<const u32x4_t *>(base + off);
-  }
-}
-
-template <int S>
-__device__ __forceinline__ void write_phase(const Chunks &ck, uint32_t tid, uint8_t *buf, uint8_t *dummy,
-                                            uint32_t pbn, const u32x4_t (&r)[S]) {
-  const uint32_t wcols = pbn * kBlockBytes / 16u, acols = pbn * 16u;
+  for (int v = 0; v < 2; ++v) {
+    const uint32_t pbn = v == 0 ? (uint32_t)kPhaseBlocks : tail_blocks;
+    const uint32_t wcols = pbn * kBlockBytes / 16u, acols = pbn * 16u;
 #pragma unroll
-  for (int s = 0; s < S; ++s) {
-    bool ok;
-    uint32_t lds_off;
-    if (s < 2) {
-      const uint32_t row = tid >> 5, col = (tid & 31u) + 32u * s;
-      ok = col < wcols;
-      lds_off = row * kWPitch + 16u * col;
-    } else {
-      const uint32_t c = (uint32_t)(s - 2) * kThreads + tid;
-      const uint32_t m = c >> 8, col = c & 255u;
-      ok = m < ck.M && col < acols;
-      lds_off = kWBytes + m * kAPitch + 16u * col;
+    for (int s = 0; s < S; ++s) {
+      if (s < 2) {
+        const uint32_t r = tid >> 5, col = (tid & 31u) + 32u * s;
+        const uint32_t row = min(r, N - 1u);
+        const bool in = col < wcols;
+        sl.src[v][s] = row * rb + 16u * (in ? col : 0u);
+        sl.dst[v][s] = in ? r * kWPitch + 16u * col : dummy;
+      } else {
+        const uint32_t c = (uint32_t)(s - 2) * kThreads + tid;
+        const uint32_t m = c >> 8, col = c & 255u;
+        const bool in = m < M && col < acols;
+        sl.src[v][s] = in ? m * K * 2u + 16u * col : 0u;
+        sl.dst[v][s] = in ? kWBytes + m * kAPitch + 16u * col : dummy;
+      }
     }
-    *reinterpret_cast<u32x4_t *>(ok ? buf + lds_off : dummy) = r[s];
   }
 }
 
@@ -197,12 +184,14 @@ __device__ __forceinline__ void mac_block(const uint8_t *blk, const uint8_t *win
   for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(d, x[r], acc[r]);
 }
 
-template <int MMAX>
+template <int MMAX, int DEPTH>
 __global__ __launch_bounds__(kThreads) void q2_0_mfma_kernel(const uint16_t *__restrict__ A,
                                                              const uint8_t *__restrict__ B,
                                                              uint16_t *__restrict__ C, uint32_t N, uint32_t K,
                                                              uint32_t M) {
   using L = Layout<MMAX>;
+  constexpr int S = L::kSlots;
+  static_assert(DEPTH % 2 == 0, "buffer parity must be a compile-time function of the ring slot");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63u;
@@ -210,16 +199,14 @@ __global__ __launch_bounds__(kThreads) void q2_0_mfma_kernel(const uint16_t *__r
   const uint32_t i = lane & 15u, g = lane >> 4;
   const uint32_t nb = K >> 7;
   const uint32_t nphase = (nb + kPhaseBlocks - 1) / kPhaseBlocks;
+  const uint32_t tail_blocks = nb - (nphase - 1u) * kPhaseBlocks;  // blocks in the last phase of a tile
   const uint32_t rb = nb * kBlockBytes;
   const uint32_t ntiles = (N + 15u) / 16u;
   // This workgroup's tiles are blockIdx.x, blockIdx.x + gridDim.x, ...; its
-  // phases form one sequence q = j * nphase + p over them, and the load ring
-  // runs across tile boundaries so the next tile's first phases are already
-  // in flight when a tile ends.
+  // phases form one sequence over them, and the load ring runs across tile
+  // boundaries so the next tile's first phases are in flight when a tile ends.
   const uint32_t my_tiles = (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x;
   const uint32_t nq = my_tiles * nphase;
-  const uint8_t *abase = reinterpret_cast<const uint8_t *>(A);
-  uint8_t *dummy = lds + L::kDummy;
 
   // zero region standing in for activation rows m >= M (visible after the
   // first phase barrier)
@@ -228,14 +215,31 @@ __global__ __launch_bounds__(kThreads) void q2_0_mfma_kernel(const uint16_t *__r
     *reinterpret_cast<u32x4_t *>(lds + L::kZero + 16u * tid) = z;
   }
 
-  const Chunks ck{B, abase, N, K, M, rb};
-  auto tile_of = [&](uint32_t j) { return blockIdx.x + j * gridDim.x; };
-  auto phase_blocks = [&](uint32_t p) { return min((uint32_t)kPhaseBlocks, nb - p * kPhaseBlocks); };
-  // Issue sequence element q (past the end: safe re-reads, stored nowhere).
-  auto issue_q = [&](uint32_t q, u32x4_t(&r)[L::kSlots]) {
+  Slots<S> sl;
+  make_slots<S>(sl, tid, N, rb, K, M, tail_blocks, L::kDummy);
+  // First row of this workgroup's j-th tile; the last tile of the matrix is
+  // shifted back so that every tile holds 16 real rows (rows it shares with
+  // the previous tile are computed with the same arithmetic and rewritten with
+  // the same bits).
+  auto tile_row = [&](uint32_t j) {
+    const uint32_t n0 = (blockIdx.x + j * gridDim.x) * 16u;
+    return N >= 16u ? min(n0, N - 16u) : 0u;
+  };
+
+  // Sequence element q is phase q % nphase of this workgroup's tile q / nphase.
+  // Past the end (q >= nq) it re-reads phase 0 of the first tile, stored nowhere.
+  auto issue_q = [&](uint32_t q, u32x4_t(&r)[S]) {
     const bool live = q < nq;
-    const uint32_t j = live ? q / nphase : 0u, p = live ? q - j * nphase : 0u;
-    issue_phase<L::kSlots>(ck, tid, tile_of(j) * 16u, p, live ? phase_blocks(p) : 0u, r);
+    const uint32_t j = live ? q / nphase : 0u;
+    const uint32_t p = live ? q - j * nphase : 0u;
+    const bool tail = p + 1u == nphase;
+    const uint8_t *wb = B + (size_t)tile_row(j) * rb + (size_t)p * kPhaseWBytes;
+    const uint8_t *ab = reinterpret_cast<const uint8_t *>(A) + (size_t)p * kAPhaseBytes;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const uint32_t off = tail ? sl.src[1][s] : sl.src[0][s];
+      r[s] = *reinterpret_cast<const u32x4_t *>((s < 2 ? wb : ab) + off);
+    }
   };
 
   // This lane's read offsets (from the LDS base) for the wave's first block of
@@ -251,28 +255,33 @@ __global__ __launch_bounds__(kThreads) void q2_0_mfma_kernel(const uint16_t *__r
   float *part = reinterpret_cast<float *>(lds + L::kPart);  // [wave][m][n]
 
   f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  // Sequence element q: store its chunks (slots of its own tile), request
-  // element q+2 into the same registers, compute on it, and finish the tile
+  // One sequence element: store its chunks into buffer `parity`, request the
+  // element DEPTH ahead into the same registers, compute, and finish the tile
   // after its last phase.
-  auto step = [&](uint32_t q, uint32_t parity, u32x4_t(&r)[L::kSlots]) {
-    const uint32_t j = q / nphase, p = q - j * nphase;
+  auto step = [&](uint32_t q, uint32_t parity, u32x4_t(&r)[S]) {
     uint8_t *buf = lds + parity * L::kBuf;
-    const uint32_t pbn = phase_blocks(p);
-    write_phase<L::kSlots>(ck, tid, buf, dummy, pbn, r);
-    issue_q(q + 2u, r);
+    const uint32_t j = q / nphase, p = q - j * nphase;
+    const bool tail = p + 1u == nphase;
+    const uint32_t pbn = tail ? tail_blocks : (uint32_t)kPhaseBlocks;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const uint32_t dst = tail ? sl.dst[1][s] : sl.dst[0][s];
+      *reinterpret_cast<u32x4_t *>(buf + dst) = r[s];
+    }
+    issue_q(q + DEPTH, r);
     __syncthreads();
     const uint8_t *a0 = lds + act + parity * act_buf;
     if (wave < pbn) mac_block(buf + blk, buf + win, a0, sel, acc);
     if (wave + kSecond < pbn)
       mac_block(buf + blk + kSecond * kBlockBytes, buf + win + kSecond * kBlockBytes, a0 + act_second, sel, acc);
-    if (p + 1u == nphase) {  // tile done: add the 8 waves' partial tiles in fixed order
+    if (tail) {  // tile done: add the 8 waves' partial tiles in fixed order
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) part[(wave * 16u + 4u * g + rr) * 16u + i] = acc[rr];
       acc = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
       __syncthreads();
       if (tid < 256u) {
         const uint32_t m = tid >> 4, col = tid & 15u;
-        const uint32_t n = tile_of(j) * 16u + col;
+        const uint32_t n = tile_row(j) + col;
         if (m < M && n < N) {
           float v = part[m * 16u + col];
           for (uint32_t w = 1; w < kWaves; ++w) v = v + part[(w * 16u + m) * 16u + col];
@@ -283,38 +292,40 @@ __global__ __launch_bounds__(kThreads) void q2_0_mfma_kernel(const uint16_t *__r
     }
   };
 
-  u32x4_t ring0[L::kSlots], ring1[L::kSlots];
-  issue_q(0u, ring0);
-  issue_q(1u, ring1);
+  u32x4_t ring[DEPTH][S];
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) issue_q((uint32_t)d, ring[d]);
   uint32_t q = 0;
-  for (; q + 2u <= nq; q += 2u) {
-    step(q, 0u, ring0);
-    step(q + 1u, 1u, ring1);
+  for (; q + DEPTH <= nq; q += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) step(q + d, (uint32_t)(d & 1), ring[d]);
   }
-  if (q < nq) step(q, 0u, ring0);
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d)
+    if (q + d < nq) step(q + d, (uint32_t)(d & 1), ring[d]);
 }
 
-template <int MMAX>
+template <int MMAX, int DEPTH>
 hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32_t K, uint32_t M,
                        hipStream_t stream) {
   // Persistent grid: as many workgroups as fit on the device at once, each
   // walking every gridDim.x-th tile.  Resolved once per process.
   static int resident = 0;
   if (resident == 0) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&q2_0_mfma_kernel<MMAX>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&(q2_0_mfma_kernel<MMAX, DEPTH>)),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, Layout<MMAX>::kTotal);
     if (e != hipSuccess) return e;
     int dev = 0, cus = 0, per_cu = 0;
     if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, q2_0_mfma_kernel<MMAX>, kThreads,
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (q2_0_mfma_kernel<MMAX, DEPTH>), kThreads,
                                                           Layout<MMAX>::kTotal)) != hipSuccess)
       return e;
     resident = (per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
   }
   const uint32_t ntiles = (N + 15) / 16;
   const uint32_t grid = ntiles < (uint32_t)resident ? ntiles : (uint32_t)resident;
-  hipLaunchKernelGGL(q2_0_mfma_kernel<MMAX>, dim3(grid), dim3(kThreads), Layout<MMAX>::kTotal, stream,
+  hipLaunchKernelGGL((q2_0_mfma_kernel<MMAX, DEPTH>), dim3(grid), dim3(kThreads), Layout<MMAX>::kTotal, stream,
                      static_cast<const uint16_t *>(A), static_cast<const uint8_t *>(B),
                      static_cast<uint16_t *>(C), N, K, M);
   return hipGetLastError();
@@ -326,10 +337,10 @@ bool q2_0_mfma_supports(uint32_t K, uint32_t m) { return ((K >> 7) % 8u) == 0 &&
 
 hipError_t launch_q2_0_mfma(const void *A, const void *B, void *C, uint32_t N, uint32_t K, uint32_t m,
                             hipStream_t stream) {
-  if (m <= 2) return launch_mmax<2>(A, B, C, N, K, m, stream);
-  if (m <= 4) return launch_mmax<4>(A, B, C, N, K, m, stream);
-  if (m <= 8) return launch_mmax<8>(A, B, C, N, K, m, stream);
-  return launch_mmax<16>(A, B, C, N, K, m, stream);
+  if (m <= 2) return launch_mmax<2, 2>(A, B, C, N, K, m, stream);
+  if (m <= 4) return launch_mmax<4, 2>(A, B, C, N, K, m, stream);
+  if (m <= 8) return launch_mmax<8, 2>(A, B, C, N, K, m, stream);
+  return launch_mmax<16, 2>(A, B, C, N, K, m, stream);
 }
 
 }  // namespace wqd
