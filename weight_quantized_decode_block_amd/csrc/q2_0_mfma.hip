@@ -1,49 +1,56 @@
 // Q2_0 ternary decode GEMV / batched GEMV on the gfx950 matrix cores.
 //
-//   C[m,n] = bf16( sum_k A[m,k] * (code[n,k] - 1) * d[n, k/128] ),  m < M <= 16
+//   C[m,n] = bf16( sum_k A[m,k] * (code[n,k] - 1) * d[n, k/128] ),  m < M <= 8
 //
 // Operation: page "gemv_q2_vec.rs", docs of q2_0_gemv_vec (M=1, 16 codes per
 // 32-bit word, A staged in shared memory, dequant (code-1)*d inside the dot
 // product) and q2_0_gemv_vec_batchm (each weight word read once per launch and
-// applied to every row; rows bit-identical to the M=1 result).  The pages'
-// batched template is issue-bound on its scalar MACs; here the MACs of all rows
-// run on v_mfma_f32_16x16x32_bf16, so the vector ALUs only decode, and M=1 runs
-// the same kernel as every other M (which is what makes rows bit-identical).
+// applied to every row of a launch of at most 8 rows; rows bit-identical to
+// the M=1 result).  The pages' kernels run the MACs on scalar FMAs; here they
+// run on v_mfma_f32_16x16x32_bf16 and the vector ALUs only decode.
 //
-// Work layout (requires K/128 to be a multiple of 8, so that every 8-block run
-// of a weight row starts on a 16-byte boundary)
-//   * A workgroup of 8 waves owns one tile of 16 weight rows and walks K in
-//     phases of up to 16 blocks (2048 k).  Each phase's bytes - the 16 rows'
-//     34-byte blocks and the M activation rows - are fetched with 16-byte loads
-//     in which consecutive lanes read consecutive addresses (a scalar base per
-//     phase plus a fixed per-lane offset), kept two phases ahead in registers
-//     and written to one of two LDS buffers; one barrier per phase separates
-//     writing a buffer from reading it.  Loads and stores are branch-free, so
-//     each store waits only for its own phase's loads: a slot with nothing to
-//     fetch re-reads an in-bounds chunk and stores it to a dummy LDS slot.
-//   * In a phase, wave w handles blocks w and w+8.  Lane l (i = l%16, g = l/16)
-//     reads code words 2g and 2g+1 of weight row i (three aligned dwords and a
-//     v_perm per word undo the block's 0/2-byte misalignment) and the 32
-//     activations k = 32g..32g+31 of row m = i (a zeroed LDS region stands in
-//     for rows m >= M); four v_mfma_f32_16x16x32_bf16, the j-th on
-//     k = 32g + 8j .. 32g + 8j + 7 of both operands, cover the block.
-//   * Decode: for a code word w, u = (w & 0x03030303) | ((w << 2) & 0x30303030)
-//     and v = ((w >> 4) & 0x03030303) | ((w >> 2) & 0x30303030) put codes
-//     4i, 4i+1 (u) and 4i+2, 4i+3 (v) in the two nibbles of byte i.  A 2-bit
-//     code zero-extended to a nibble is the FP4 E2M1 value c/2, so the hardware
-//     FP4->BF16 conversion with scale 2 gives the exact BF16 pair (c_j, c_j+1)
-//     in k order, matching the activations' natural order.
-//   * The -1 of (code-1): a fifth MFMA chain per block multiplies the
-//     activations by an all -1 operand, giving -sum a over the block in the
-//     accumulator layout; it seeds the block's chain, which then ends at
-//     sum a*c - sum a = sum a*(c-1).  Products a*c are exact (c in 0..3).
+// Work layout (requires K/128 to be a multiple of 8)
+//   * A tile is 8 weight rows over the whole of K.  One MFMA covers two
+//     consecutive 128-k blocks (a block pair) of the tile: its 16 columns are
+//     (block half h, weight row r) = column 8h + r, and its 16 rows are (block
+//     half h, activation row m) = row 8h + m.  Output (8h+m, 8h+r) is the dot
+//     product of activation row m with weight row r over block half h; the
+//     two off-diagonal quadrants mix different blocks and are never used.
+//     Eight rows per tile (instead of sixteen) gives twice as many tiles,
+//     which spreads a matrix far more evenly over 256 compute units, and still
+//     leaves room for all 8 activation rows of a batched launch.
+//   * A workgroup of 8 waves walks its tiles (blockIdx.x, + gridDim.x, ...).
+//     Wave w owns block pairs w, w+8, w+16, ... of every tile and works on
+//     its own: for each pair it fetches the 8 rows' 68 bytes (5 aligned
+//     16-byte chunks per row, one load per lane), keeps DEPTH pairs in flight
+//     in registers, and passes them through its own LDS buffers to the lanes
+//     that need them.  No barrier separates a wave's loads from its compute;
+//     the 8 waves meet once per tile, to add their partial sums.
+//   * Activations: all M rows of A are copied into LDS once per workgroup.
+//     Each group of four consecutive activations is stored in the order
+//     (a0, a2, a1, a3), the order the decode below produces codes in.  Rows
+//     m >= M read a zero region.
+//   * Decode: for a code word w, u = w & 0x33333333 holds codes 4i and 4i+2
+//     in the two nibbles of byte i, v = (w >> 2) & 0x33333333 codes 4i+1 and
+//     4i+3.  A 2-bit code zero-extended to a nibble is the FP4 E2M1 value
+//     c/2, so the hardware FP4->BF16 conversion with scale 2 gives exact BF16
+//     pairs (c_4i, c_4i+2) and (c_4i+1, c_4i+3).
+//   * The -1 of (code-1): for every block and activation row, an MFMA chain
+//     of the activations against an all -1 operand gives -sum a over the
+//     block.  The wave that owns a block pair computes it on its workgroup's
+//     first tile and keeps it in LDS for the later ones.  It seeds that
+//     block's chain, which then ends at sum a*c - sum a = sum a*(c-1)
+//     (products a*c are exact, c in 0..3).
 //   * Scale: acc += d[n] * chain once per block (fma), never per element.
-//   * The 8 waves' partial tiles are added in LDS in fixed wave order and rows
-//     m < M are stored as BF16, round to nearest even.
+//   * At the end of a tile the 16 partial sums of an output (8 waves x 2
+//     block halves) are added in LDS in fixed order and rows m < M are stored
+//     as BF16, round to nearest even.  The last tile is shifted back to start
+//     at N - 8, so every tile holds 8 real weight rows.
 //
 // Bit-identity across row counts: an output's value depends only on its own
-// activation row, its weight row and the fixed block / wave order; activation
-// rows >= M are zero operands.  So M=1 and every batched M give the same bits.
+// activation row, its weight row and the fixed block / wave / half order;
+// activation row m always sits in MFMA rows m and 8 + m.  So M=1 and every
+// batched M give the same bits.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -55,30 +62,20 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
 
 constexpr int kBlockBytes = 34;
+constexpr int kRows = 8;                                  // weight rows per tile
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kPhaseBlocks = 16;                          // blocks per phase
-constexpr int kPhaseWBytes = kPhaseBlocks * kBlockBytes;  // 544 bytes of one weight row per phase
-constexpr int kWPitch = kPhaseWBytes + 16;                // LDS row pitch (bank spread)
-constexpr int kWBytes = 16 * kWPitch;                     // weight part of a buffer
+constexpr int kSlots8 = 8;  // accumulation slots of a tile's block pairs
+constexpr int kPhaseBlocks = 16;                          // blocks per phase (8 waves x 2)
+constexpr int kPhaseRowBytes = kPhaseBlocks * kBlockBytes;  // 544 bytes of one weight row per phase
+constexpr int kWPitch = kPhaseRowBytes + 16;              // LDS row pitch (bank spread)
+constexpr int kWBytes = kRows * kWPitch;                  // weight part of a buffer
 constexpr int kAPhaseBytes = kPhaseBlocks * 256;          // 4096 bytes of one activation row per phase
-constexpr int kAPitch = kAPhaseBytes + 16;                // LDS pitch of an activation row
-constexpr int kSecond = 8;                                // a wave's second block of a phase: w + 8
-
-// LDS: [buffer 0][buffer 1][zero rows: kAPhaseBytes][partial tiles: kWaves x
-// 16 x 16 floats]; a buffer holds 16 weight-row segments, MMAX activation-row
-// segments and a 16-byte dummy slot at kDummy (buffer-relative).
-template <int MMAX>
-struct Layout {
-  static constexpr int kSlots = 2 + (MMAX * (kAPhaseBytes / 16) + kThreads - 1) / kThreads;
-  static constexpr int kDummy = kWBytes + MMAX * kAPitch;
-  static constexpr int kBuf = kDummy + 16;
-  static constexpr int kZero = 2 * kBuf;
-  static constexpr int kPart = kZero + kAPhaseBytes;
-  static constexpr int kTotal = kPart + kWaves * 256 * 4;
-};
+constexpr int kAPitch = kAPhaseBytes + 16;                // LDS pitch of a per-phase activation row
+constexpr uint32_t kLdsMax = 160u * 1024u;                // LDS per compute unit on gfx950
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -92,35 +89,77 @@ __device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t v) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 2.0f, BYTE));
 }
 
-// The 16 codes of word w as two 8-element BF16 operands (codes 0..7, 8..15).
+// The 16 codes of word w as two 8-element BF16 operands, in the order
+// (c0 c2 c1 c3 c4 c6 c5 c7) and (c8 c10 c9 c11 c12 c14 c13 c15).
 __device__ __forceinline__ void decode_word(uint32_t w, bf16x8_t &lo, bf16x8_t &hi) {
-  const uint32_t u = (w & 0x03030303u) | ((w << 2) & 0x30303030u);
-  const uint32_t v = ((w >> 4) & 0x03030303u) | ((w >> 2) & 0x30303030u);
+  const uint32_t u = w & 0x33333333u;
+  const uint32_t v = (w >> 2) & 0x33333333u;
   u32x4_t a, b;
-  a.x = fp4x2_to_bf16x2<0>(u);  // c0, c1
-  a.y = fp4x2_to_bf16x2<0>(v);  // c2, c3
-  a.z = fp4x2_to_bf16x2<1>(u);  // c4, c5
-  a.w = fp4x2_to_bf16x2<1>(v);  // c6, c7
-  b.x = fp4x2_to_bf16x2<2>(u);  // c8, c9
-  b.y = fp4x2_to_bf16x2<2>(v);  // c10, c11
-  b.z = fp4x2_to_bf16x2<3>(u);  // c12, c13
-  b.w = fp4x2_to_bf16x2<3>(v);  // c14, c15
+  a.x = fp4x2_to_bf16x2<0>(u);
+  a.y = fp4x2_to_bf16x2<0>(v);
+  a.z = fp4x2_to_bf16x2<1>(u);
+  a.w = fp4x2_to_bf16x2<1>(v);
+  b.x = fp4x2_to_bf16x2<2>(u);
+  b.y = fp4x2_to_bf16x2<2>(v);
+  b.z = fp4x2_to_bf16x2<3>(u);
+  b.w = fp4x2_to_bf16x2<3>(v);
   lo = __builtin_bit_cast(bf16x8_t, a);
   hi = __builtin_bit_cast(bf16x8_t, b);
 }
 
-// The 16-byte chunk slots of a thread.  Slots 0-1 carry weight chunks: row
-// r = tid/32 of the tile, column col = tid%32 + 32s of the row's phase segment
-// (34 columns in a full phase).  Slots 2.. carry activation chunks: c =
-// (s-2)*512 + tid, row m = c/256, column c%256 (256 columns in a full phase).
-// Every slot keeps two precomputed (source offset, LDS destination) pairs: one
-// for full phases and one for the K tail's shorter phase.  A column past a
-// phase's end re-reads an in-bounds column and goes to the dummy LDS slot; an
-// activation row past M likewise.  A tile always has 16 real rows when N >= 16
-// (the last tile is shifted back to start at N - 16); for N < 16 a row past N
-// re-reads row N - 1 and its columns are never stored.  Source offsets are
-// relative to a per-phase scalar base, so issuing a phase costs one select per
-// slot.
+// Eight consecutive activations (a0..a7) reordered to (a0 a2 a1 a3 a4 a6 a5 a7).
+__device__ __forceinline__ u32x4_t permute_acts(u32x4_t x) {
+  u32x4_t y;
+  y.x = __builtin_amdgcn_perm(x.y, x.x, 0x05040100u);
+  y.y = __builtin_amdgcn_perm(x.y, x.x, 0x07060302u);
+  y.z = __builtin_amdgcn_perm(x.w, x.z, 0x05040100u);
+  y.w = __builtin_amdgcn_perm(x.w, x.z, 0x07060302u);
+  return y;
+}
+
+// -sum over a block of each MFMA row's activations, in the MFMA accumulator
+// layout (every column holds the same value).
+__device__ __forceinline__ f32x4_t neg_sum_chain(const bf16x8_t (&a)[4]) {
+  const u32x4_t m1 = {0xbf80bf80u, 0xbf80bf80u, 0xbf80bf80u, 0xbf80bf80u};  // bf16 -1.0
+  const bf16x8_t neg1 = __builtin_bit_cast(bf16x8_t, m1);
+  f32x4_t x = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], neg1, x, 0, 0, 0);
+  return x;
+}
+
+// ---------------------------------------------------------------------------
+// Per-phase kernel: for activations too large to keep in LDS.  Same unit
+// assignment, seeds, chains and reduction order as the pairs kernel below, so
+// both give the same bits.  A workgroup walks its tiles in phases of 16
+// blocks: each phase's 8 x 544 weight bytes and 16 blocks of every activation
+// row are fetched with 16-byte loads in which consecutive lanes read
+// consecutive addresses, kept DEPTH phases ahead in registers and written to
+// one of two LDS buffers (one barrier per phase); wave w computes block pair
+// w of the phase (pair 8p + w of the tile) with its seed computed in line.
+// ---------------------------------------------------------------------------
+// LDS: [buffer 0][buffer 1][zero rows: 256][partial tiles: 2 x kWaves x 2 x
+// MMAX x 8 floats].  A buffer holds the phase's weight rows, MMAX
+// activation-row segments and a 16-byte dummy slot at kDummy
+// (buffer-relative).
+template <int MMAX>
+struct PhaseLayout {
+  static constexpr int kSlots = 1 + (MMAX * (kAPhaseBytes / 16) + kThreads - 1) / kThreads;
+  static constexpr int kDummy = kWBytes + MMAX * kAPitch;
+  static constexpr int kBuf = kDummy + 16;
+  static constexpr int kZero = 2 * kBuf;
+  static constexpr int kPart = kZero + 256;
+  static constexpr int kFixed = kPart + 2 * kWaves * 2 * MMAX * kRows * 4;
+};
+
+// The 16-byte chunk slots of a thread.  Slot 0 carries weight chunks: row
+// r = tid / c of the tile, column tid % c of the row's phase segment, c = 34
+// chunks in a full phase (17 in a half-length last phase).  Slots 1.. carry
+// per-phase activation chunks: k = (s-1)*512 + tid, row m = k/256, column
+// k%256.  Every slot keeps two precomputed (source offset, LDS destination)
+// pairs: one for full phases and one for the K tail's phase.  A chunk with
+// nothing to fetch re-reads an in-bounds chunk and goes to the dummy LDS slot.
+// For N < 8 a row past N re-reads row N - 1 and its outputs are never stored.
 template <int S>
 struct Slots {
   uint32_t src[2][S];  // [full, tail]
@@ -134,96 +173,61 @@ __device__ __forceinline__ void make_slots(Slots<S> &sl, uint32_t tid, uint32_t 
   for (int v = 0; v < 2; ++v) {
     const uint32_t pbn = v == 0 ? (uint32_t)kPhaseBlocks : tail_blocks;
     const uint32_t wcols = pbn * kBlockBytes / 16u, acols = pbn * 16u;
+    {
+      const uint32_t r = tid / wcols, col = tid - r * wcols;
+      const bool in = r < (uint32_t)kRows;
+      const uint32_t row = in ? min(r, N - 1u) : 0u;
+      sl.src[v][0] = in ? row * rb + 16u * col : 0u;
+      sl.dst[v][0] = in ? r * kWPitch + 16u * col : dummy;
+    }
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      if (s < 2) {
-        const uint32_t r = tid >> 5, col = (tid & 31u) + 32u * s;
-        const uint32_t row = min(r, N - 1u);
-        const bool in = col < wcols;
-        sl.src[v][s] = row * rb + 16u * (in ? col : 0u);
-        sl.dst[v][s] = in ? r * kWPitch + 16u * col : dummy;
-      } else {
-        const uint32_t c = (uint32_t)(s - 2) * kThreads + tid;
-        const uint32_t m = c >> 8, col = c & 255u;
-        const bool in = m < M && col < acols;
-        sl.src[v][s] = in ? m * K * 2u + 16u * col : 0u;
-        sl.dst[v][s] = in ? kWBytes + m * kAPitch + 16u * col : dummy;
-      }
+    for (int s = 1; s < S; ++s) {
+      const uint32_t c = (uint32_t)(s - 1) * kThreads + tid;
+      const uint32_t m = c >> 8, col = c & 255u;
+      const bool in = m < M && col < acols;
+      sl.src[v][s] = in ? m * K * 2u + 16u * col : 0u;
+      sl.dst[v][s] = in ? kWBytes + m * kAPitch + 16u * col : dummy;
     }
   }
 }
 
-// One block into acc.  `blk` points at the block in LDS (its fp16 scale),
-// `win` at this lane's aligned code window, `act` at its 64 bytes of
-// activations (or the zero region); `sel` undoes the block's misalignment.
-__device__ __forceinline__ void mac_block(const uint8_t *blk, const uint8_t *win, const uint8_t *act, uint32_t sel,
-                                          f32x4_t &acc) {
-  const u32x4_t *pa = reinterpret_cast<const u32x4_t *>(act);
-  bf16x8_t a[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) a[j] = __builtin_bit_cast(bf16x8_t, pa[j]);
-  const u32x4_t m1 = {0xbf80bf80u, 0xbf80bf80u, 0xbf80bf80u, 0xbf80bf80u};  // bf16 -1.0
-  const bf16x8_t neg1 = __builtin_bit_cast(bf16x8_t, m1);
-  f32x4_t x = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], neg1, x, 0, 0, 0);
-
-  const uint32_t *pw = reinterpret_cast<const uint32_t *>(win);
-  const uint32_t c0 = pw[0], c1 = pw[1], c2 = pw[2];
-  const uint32_t w0 = __builtin_amdgcn_perm(c1, c0, sel);
-  const uint32_t w1 = __builtin_amdgcn_perm(c2, c1, sel);
-  const float d = (float)*reinterpret_cast<const _Float16 *>(blk);
-  bf16x8_t b0, b1, b2, b3;
-  decode_word(w0, b0, b1);
-  decode_word(w1, b2, b3);
-  x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b0, x, 0, 0, 0);
-  x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], b1, x, 0, 0, 0);
-  x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2], b2, x, 0, 0, 0);
-  x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[3], b3, x, 0, 0, 0);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(d, x[r], acc[r]);
-}
-
 template <int MMAX, int DEPTH>
-__global__ __launch_bounds__(kThreads) void q2_0_mfma_kernel(const uint16_t *__restrict__ A,
-                                                             const uint8_t *__restrict__ B,
-                                                             uint16_t *__restrict__ C, uint32_t N, uint32_t K,
-                                                             uint32_t M) {
-  using L = Layout<MMAX>;
+__global__ __launch_bounds__(kThreads) void q2_0_phase_kernel(const uint16_t *__restrict__ A,
+                                                              const uint8_t *__restrict__ B,
+                                                              uint16_t *__restrict__ C, uint32_t N, uint32_t K,
+                                                              uint32_t M) {
+  using L = PhaseLayout<MMAX>;
   constexpr int S = L::kSlots;
+  constexpr int NF = MMAX < 4 ? MMAX : 4;  // accumulator rows that can hold outputs
   static_assert(DEPTH % 2 == 0, "buffer parity must be a compile-time function of the ring slot");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t i = lane & 15u, g = lane >> 4;
+  const uint32_t h = i >> 3, rw = i & 7u;  // MFMA column i = (block half h, weight row rw)
   const uint32_t nb = K >> 7;
   const uint32_t nphase = (nb + kPhaseBlocks - 1) / kPhaseBlocks;
-  const uint32_t tail_blocks = nb - (nphase - 1u) * kPhaseBlocks;  // blocks in the last phase of a tile
+  const uint32_t tail_blocks = nb - (nphase - 1u) * kPhaseBlocks;  // 8 or 16
   const uint32_t rb = nb * kBlockBytes;
-  const uint32_t ntiles = (N + 15u) / 16u;
+  const uint32_t ntiles = N >= (uint32_t)kRows ? (N + kRows - 1u) / kRows : 1u;
   // This workgroup's tiles are blockIdx.x, blockIdx.x + gridDim.x, ...; its
   // phases form one sequence over them, and the load ring runs across tile
   // boundaries so the next tile's first phases are in flight when a tile ends.
   const uint32_t my_tiles = (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x;
   const uint32_t nq = my_tiles * nphase;
 
-  // zero region standing in for activation rows m >= M (visible after the
-  // first phase barrier)
-  if (tid < (uint32_t)kAPhaseBytes / 16u) {
+  // zero region standing in for activation rows m >= M
+  if (tid < 16u) {
     const u32x4_t z = {0u, 0u, 0u, 0u};
     *reinterpret_cast<u32x4_t *>(lds + L::kZero + 16u * tid) = z;
   }
 
   Slots<S> sl;
   make_slots<S>(sl, tid, N, rb, K, M, tail_blocks, L::kDummy);
-  // First row of this workgroup's j-th tile; the last tile of the matrix is
-  // shifted back so that every tile holds 16 real rows (rows it shares with
-  // the previous tile are computed with the same arithmetic and rewritten with
-  // the same bits).
   auto tile_row = [&](uint32_t j) {
-    const uint32_t n0 = (blockIdx.x + j * gridDim.x) * 16u;
-    return N >= 16u ? min(n0, N - 16u) : 0u;
+    const uint32_t n0 = (blockIdx.x + j * gridDim.x) * (uint32_t)kRows;
+    return N >= (uint32_t)kRows ? min(n0, N - (uint32_t)kRows) : 0u;
   };
 
   // Sequence element q is phase q % nphase of this workgroup's tile q / nphase.
@@ -233,28 +237,58 @@ __global__ __launch_bounds__(kThreads) void q2_0_mfma_kernel(const uint16_t *__r
     const uint32_t j = live ? q / nphase : 0u;
     const uint32_t p = live ? q - j * nphase : 0u;
     const bool tail = p + 1u == nphase;
-    const uint8_t *wb = B + (size_t)tile_row(j) * rb + (size_t)p * kPhaseWBytes;
+    const uint8_t *wb = B + (size_t)tile_row(j) * rb + (size_t)p * kPhaseRowBytes;
     const uint8_t *ab = reinterpret_cast<const uint8_t *>(A) + (size_t)p * kAPhaseBytes;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       const uint32_t off = tail ? sl.src[1][s] : sl.src[0][s];
-      r[s] = *reinterpret_cast<const u32x4_t *>((s < 2 ? wb : ab) + off);
+      r[s] = *reinterpret_cast<const u32x4_t *>((s == 0 ? wb : ab) + off);
     }
   };
 
-  // This lane's read offsets (from the LDS base) for the wave's first block of
-  // a phase in buffer 0; buffer 1 adds kBuf, the second block (w + 8) adds
-  // 8 blocks.  Blocks w and w+8 have the same 0/2-byte misalignment.
-  const uint32_t blk = i * kWPitch + wave * kBlockBytes;
-  const uint32_t win = (blk + 8u * g) & ~3u;  // code bytes start at +2 (even block) or +4 (odd)
-  const uint32_t sel = (blk & 2u) ? 0x07060504u : 0x05040302u;
-  const bool a_ok = i < M;
-  const uint32_t act = a_ok ? kWBytes + i * kAPitch + wave * 256u + 64u * g : L::kZero + 64u * g;
-  const uint32_t act_buf = a_ok ? (uint32_t)L::kBuf : 0u;  // the zero region is shared by both buffers
-  const uint32_t act_second = a_ok ? kSecond * 256u : 0u;
-  float *part = reinterpret_cast<float *>(lds + L::kPart);  // [wave][m][n]
+  // This lane's MFMA operands within a phase: weight row rw of block 2*wave+h
+  // (its fp16 scale at wblk; its 8 code bytes inside the aligned 3-dword
+  // window at wwin, which `sel` extracts), and activation row rw of the same
+  // block (or the zero region).
+  const uint32_t wblk = rw * kWPitch + 34u * h + 68u * wave;
+  const uint32_t wwin = rw * kWPitch + 32u * h + 8u * g + 68u * wave;  // code bytes at +2 (h = 0) or +4 (h = 1)
+  const uint32_t sel = h ? 0x07060504u : 0x05040302u;
+  const bool a_ok = rw < M;
+  const uint32_t a_lane =
+      a_ok ? (uint32_t)kWBytes + rw * kAPitch + (2u * wave + h) * 256u + 64u * g : (uint32_t)L::kZero + 64u * g;
+  const uint32_t a_buf = a_ok ? (uint32_t)L::kBuf : 0u;  // + per buffer
+  const bool lane_out = (g >> 1) == h;  // this lane's accumulator rows match its column's block half
+  float *part = reinterpret_cast<float *>(lds + L::kPart);  // [tile parity][wave][half][m][r]
+
+  u32x4_t ring[DEPTH][S];
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) issue_q((uint32_t)d, ring[d]);
 
   f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  // The wave's block pair of the phase in buffer `parity` into acc.
+  auto unit = [&](uint32_t parity) {
+    const uint8_t *buf = lds + parity * L::kBuf;
+    const uint8_t *act = lds + a_lane + parity * a_buf;
+    bf16x8_t a[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = *reinterpret_cast<const bf16x8_t *>(act + 16 * j);
+    f32x4_t x = neg_sum_chain(a);
+    const uint32_t *pw = reinterpret_cast<const uint32_t *>(buf + wwin);
+    const uint32_t c0 = pw[0], c1 = pw[1], c2 = pw[2];
+    const uint32_t w0 = __builtin_amdgcn_perm(c1, c0, sel);
+    const uint32_t w1 = __builtin_amdgcn_perm(c2, c1, sel);
+    const _Float16 d = *reinterpret_cast<const _Float16 *>(buf + wblk);
+    bf16x8_t b0, b1, b2, b3;
+    decode_word(w0, b0, b1);
+    decode_word(w1, b2, b3);
+    x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b0, x, 0, 0, 0);
+    x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], b1, x, 0, 0, 0);
+    x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2], b2, x, 0, 0, 0);
+    x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[3], b3, x, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < NF; ++r) acc[r] = __builtin_fmaf((float)d, x[r], acc[r]);
+  };
+
   // One sequence element: store its chunks into buffer `parity`, request the
   // element DEPTH ahead into the same registers, compute, and finish the tile
   // after its last phase.
@@ -262,39 +296,40 @@ __global__ __launch_bounds__(kThreads) void q2_0_mfma_kernel(const uint16_t *__r
     uint8_t *buf = lds + parity * L::kBuf;
     const uint32_t j = q / nphase, p = q - j * nphase;
     const bool tail = p + 1u == nphase;
-    const uint32_t pbn = tail ? tail_blocks : (uint32_t)kPhaseBlocks;
+    const uint32_t npairs = tail ? tail_blocks >> 1 : (uint32_t)kPhaseBlocks / 2u;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       const uint32_t dst = tail ? sl.dst[1][s] : sl.dst[0][s];
-      *reinterpret_cast<u32x4_t *>(buf + dst) = r[s];
+      *reinterpret_cast<u32x4_t *>(buf + dst) = s == 0 ? r[s] : permute_acts(r[s]);
     }
     issue_q(q + DEPTH, r);
     __syncthreads();
-    const uint8_t *a0 = lds + act + parity * act_buf;
-    if (wave < pbn) mac_block(buf + blk, buf + win, a0, sel, acc);
-    if (wave + kSecond < pbn)
-      mac_block(buf + blk + kSecond * kBlockBytes, buf + win + kSecond * kBlockBytes, a0 + act_second, sel, acc);
-    if (tail) {  // tile done: add the 8 waves' partial tiles in fixed order
+    if (wave < npairs) unit(parity);
+    if (tail) {  // tile done: add the 16 partial sums of each output in fixed order
+      const uint32_t par = j & 1u;
+      if (lane_out) {
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) part[(wave * 16u + 4u * g + rr) * 16u + i] = acc[rr];
+        for (int rr = 0; rr < NF; ++rr) {
+          const uint32_t m = 4u * (g & 1u) + rr;
+          if (m < M) part[(((par * kWaves + wave) * 2u + h) * MMAX + m) * kRows + rw] = acc[rr];
+        }
+      }
       acc = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
       __syncthreads();
-      if (tid < 256u) {
-        const uint32_t m = tid >> 4, col = tid & 15u;
+      if (tid < M * (uint32_t)kRows) {
+        const uint32_t m = tid >> 3, col = tid & 7u;
         const uint32_t n = tile_row(j) + col;
-        if (m < M && n < N) {
-          float v = part[m * 16u + col];
-          for (uint32_t w = 1; w < kWaves; ++w) v = v + part[(w * 16u + m) * 16u + col];
+        if (n < N) {
+          const float *pp = part + (par * kWaves * 2u * MMAX + m) * kRows + col;
+          float v = pp[0];
+          for (uint32_t k = 1; k < 2u * kWaves; ++k) v = v + pp[k * MMAX * kRows];
           C[(size_t)m * N + n] = f32_to_bf16_rne(v);
         }
       }
-      // the next write of `part` comes after at least one more phase barrier
+      // the next write of this parity's partials comes after another tile's barriers
     }
   };
 
-  u32x4_t ring[DEPTH][S];
-#pragma unroll
-  for (int d = 0; d < DEPTH; ++d) issue_q((uint32_t)d, ring[d]);
   uint32_t q = 0;
   for (; q + DEPTH <= nq; q += DEPTH) {
 #pragma unroll
@@ -305,42 +340,301 @@ __global__ __launch_bounds__(kThreads) void q2_0_mfma_kernel(const uint16_t *__r
     if (q + d < nq) step(q + d, (uint32_t)(d & 1), ring[d]);
 }
 
-template <int MMAX, int DEPTH>
+
+// ---------------------------------------------------------------------------
+// Resident-activation kernel (the usual case): per-wave block pairs.
+// ---------------------------------------------------------------------------
+// LDS: [zero rows: 256][partial tiles: 2 x 8 slots x 2 x MMAX x 8 floats]
+// [seeds: nb x 8 floats][A: M rows, pitch 2K + 16].
+template <int MMAX>
+struct PairLayout {
+  static constexpr int kZero = 0;
+  static constexpr int kPart = kZero + 256;
+  static constexpr int kFixed = kPart + 2 * kSlots8 * 2 * MMAX * kRows * 4;
+};
+
+template <int MMAX>
+constexpr size_t pair_lds_bytes(uint32_t M, uint32_t K) {
+  return (size_t)PairLayout<MMAX>::kFixed + (size_t)(K >> 7) * 32u + (size_t)M * (2u * K + 16u);
+}
+
+// One block pair's bytes for this lane: the aligned 3-dword window holding
+// its 8 code bytes and the dword holding its fp16 scale (low half).
+struct PairRegs {
+  u32x3_t w;
+  uint32_t d;
+};
+
+// NW waves per workgroup (4 or 8).  Pair p of a tile belongs to accumulation
+// slot p % 8 whatever NW is: wave w owns pairs w, w + NW, ... and keeps one
+// accumulator per slot it owns, so the sums are those of the per-phase kernel.
+// Weight bytes go straight from memory to the lanes that use them (buffer
+// loads bounded by the matrix size): lane (h, r, g) reads 12 bytes at
+// 68p + 32h + 8g of weight row r and 2 bytes (the scale) at 68p + 34h.
+template <int MMAX, int NW, int DEPTH>
+__global__ __launch_bounds__(64 * NW) void q2_0_pairs_kernel(const uint16_t *__restrict__ A,
+                                                             const uint8_t *__restrict__ B,
+                                                             uint16_t *__restrict__ C, uint32_t N, uint32_t K,
+                                                             uint32_t M) {
+  using L = PairLayout<MMAX>;
+  constexpr int NF = MMAX < 4 ? MMAX : 4;  // accumulator rows that can hold outputs
+  constexpr int NACC = kSlots8 / NW;       // accumulation slots per wave
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const uint32_t tid = threadIdx.x;
+  const uint32_t lane = tid & 63u;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t i = lane & 15u, g = lane >> 4;
+  const uint32_t h = i >> 3, rw = i & 7u;  // MFMA column i = (block half h, weight row rw)
+  const uint32_t nb = K >> 7, npairs = nb >> 1;
+  const uint32_t rb = nb * kBlockBytes;
+  const uint32_t ntiles = N >= (uint32_t)kRows ? (N + kRows - 1u) / kRows : 1u;
+  const uint32_t my_tiles = (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x;
+  // pairs of a tile owned by this wave: wave, wave + NW, ...  A wave that
+  // owns none (K = 1024, NW = 8) still runs one unit per tile that computes
+  // nothing, so every wave meets the once-per-tile barrier.
+  const uint32_t upw = npairs > wave ? (npairs - wave + NW - 1) / NW : 1u;
+  const uint32_t nq = my_tiles * upw;
+  const uint32_t seed_off = L::kFixed;
+  const uint32_t a_off = L::kFixed + nb * 32u;
+  const uint32_t a_pitch = 2u * K + 16u;
+
+  if (tid < 16u) {  // zero region standing in for activation rows m >= M
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4_t *>(lds + L::kZero + 16u * tid) = z;
+  }
+  const __amdgpu_buffer_rsrc_t wrsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(B), (short)0, (int)(N * rb), 0x00020000);
+  const uint32_t row_off = min(rw, N - 1u) * rb;  // rows past N (N < 8) re-read row N - 1
+  const uint32_t w_voff = row_off + 32u * h + 8u * g;
+  const uint32_t d_voff = row_off + 34u * h;
+  // Unit q of this wave is pair wave + NW*u of tile j (q = j * upw + u).
+  // Two wave-uniform cursors walk the units in order, one for the loads
+  // (DEPTH units ahead) and one for the compute, so the per-unit bookkeeping
+  // is a few scalar adds.  Past the end the load cursor re-reads the wave's
+  // first pair (clamped into the row), which is never used.
+  struct Cursor {
+    uint32_t q, u, j, row;  // unit, pair index within the tile, tile index, tile's first row
+  };
+  const uint32_t row_step = (uint32_t)kRows * gridDim.x;
+  const uint32_t row_last = N >= (uint32_t)kRows ? N - (uint32_t)kRows : 0u;
+  auto first_row = [&]() { return N >= (uint32_t)kRows ? min(blockIdx.x * (uint32_t)kRows, row_last) : 0u; };
+  auto advance = [&](Cursor &c) {
+    ++c.q;
+    if (++c.u == upw) {
+      c.u = 0;
+      ++c.j;
+      c.row = N >= (uint32_t)kRows ? min(c.row + row_step, row_last) : 0u;
+    }
+  };
+  const uint32_t soff_first = first_row() * rb + 68u * min(wave, npairs - 1u);
+  Cursor ld = {0u, 0u, 0u, first_row()};
+  auto issue_next = [&]() {
+    const uint32_t p = min(wave + NW * ld.u, npairs - 1u);
+    const uint32_t soff = ld.q < nq ? ld.row * rb + 68u * p : soff_first;
+    PairRegs r;
+    r.w = __builtin_amdgcn_raw_buffer_load_b96(wrsrc, w_voff, soff, 0);
+    r.d = __builtin_amdgcn_raw_buffer_load_b16(wrsrc, d_voff, soff, 0);
+    advance(ld);
+    return r;
+  };
+
+  const bool a_ok = rw < M;
+  const uint32_t a_lane = a_ok ? a_off + rw * a_pitch + h * 256u + 64u * g : (uint32_t)L::kZero + 64u * g;
+  const uint32_t a_stride = a_ok ? 512u : 0u;  // per pair
+  // seed of MFMA rows 4g..4g+3 = (half g/2, activation rows 4(g%2)..+3)
+  const uint32_t s_lane = seed_off + (g >> 1) * 32u + 16u * (g & 1u);  // + 64 per pair
+  // the 8 code bytes sit at byte 2 (h = 0) or 4 (h = 1) of the window
+  const uint32_t sel = h ? 0x07060504u : 0x05040302u;
+  const bool lane_out = (g >> 1) == h;
+  float *part = reinterpret_cast<float *>(lds + L::kPart);  // [tile parity][slot][half][m][r]
+
+  // ---- prologue: A into LDS (permuted) while the first DEPTH pairs are in flight
+  PairRegs ring[DEPTH];
+  {
+    constexpr int U = 1024 / (64 * NW);  // chunks per thread per round (1024 per workgroup)
+    const uint32_t cpr = K >> 3;
+    const uint32_t total = M * cpr;
+    const uint32_t spare = tid % total;  // in-bounds chunk re-read by idle slots
+    u32x4_t av[U];
+    uint32_t adst[U];
+    auto a_load = [&](uint32_t base) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t c = base + (uint32_t)u * (64u * NW) + tid;
+        const bool in = c < total;
+        const uint32_t cc = in ? c : spare;
+        const uint32_t m = cc / cpr, col = cc - m * cpr;
+        av[u] = *reinterpret_cast<const u32x4_t *>(reinterpret_cast<const uint8_t *>(A) + (size_t)cc * 16u);
+        adst[u] = in ? a_off + m * a_pitch + 16u * col : (uint32_t)L::kPart;  // idle: into the partials
+      }
+    };
+    auto a_store = [&]() {
+#pragma unroll
+      for (int u = 0; u < U; ++u) *reinterpret_cast<u32x4_t *>(lds + adst[u]) = permute_acts(av[u]);
+    };
+    a_load(0u);
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) ring[d] = issue_next();
+    a_store();
+    for (uint32_t base = U * (64u * NW); base < total; base += U * (64u * NW)) {
+      a_load(base);
+      a_store();
+    }
+    __syncthreads();
+  }
+
+  f32x4_t acc[NACC];
+#pragma unroll
+  for (int k = 0; k < NACC; ++k) acc[k] = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
+  // Pair p of the tile into acc.  On the workgroup's first tile the pair's
+  // seeds are computed and kept in LDS (only this wave ever uses them); later
+  // tiles read them back.
+  auto unit = [&](const PairRegs &r, uint32_t p, bool first, f32x4_t &sum) {
+    const uint8_t *act = lds + a_lane + a_stride * p;
+    bf16x8_t a[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = *reinterpret_cast<const bf16x8_t *>(act + 16 * j);
+    f32x4_t x;
+    if (first) {
+      x = neg_sum_chain(a);
+      if (i == 0u) *reinterpret_cast<f32x4_t *>(lds + s_lane + 64u * p) = x;
+    } else {
+      x = *reinterpret_cast<const f32x4_t *>(lds + s_lane + 64u * p);
+    }
+    const uint32_t w0 = __builtin_amdgcn_perm(r.w.y, r.w.x, sel);
+    const uint32_t w1 = __builtin_amdgcn_perm(r.w.z, r.w.y, sel);
+    const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)r.d);
+    bf16x8_t b0, b1, b2, b3;
+    decode_word(w0, b0, b1);
+    decode_word(w1, b2, b3);
+    x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b0, x, 0, 0, 0);
+    x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], b1, x, 0, 0, 0);
+    x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2], b2, x, 0, 0, 0);
+    x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[3], b3, x, 0, 0, 0);
+#pragma unroll
+    for (int rr = 0; rr < NF; ++rr) sum[rr] = __builtin_fmaf((float)d, x[rr], sum[rr]);
+  };
+
+  // One unit: compute from its ring registers, then request the unit DEPTH
+  // ahead into the same registers (reusing them in place keeps the ring free
+  // of register copies, which would wait for loads still in flight), and
+  // after the wave's last pair of the tile add the tile's partial sums.
+  Cursor cc = {0u, 0u, 0u, first_row()};
+  auto step = [&](PairRegs &r) {
+    const uint32_t j = cc.j, u = cc.u, row = cc.row;
+    const uint32_t p = wave + NW * u;
+    if (p < npairs) {
+      if (NACC == 1 || (u & 1u) == 0u)
+        unit(r, p, j == 0u, acc[0]);
+      else
+        unit(r, p, j == 0u, acc[NACC - 1]);
+    }
+    r = issue_next();
+    advance(cc);
+    if (u + 1u == upw) {  // tile done: add the 16 partial sums of each output in fixed order
+      const uint32_t par = j & 1u;
+      if (lane_out) {
+#pragma unroll
+        for (int k = 0; k < NACC; ++k) {
+          const uint32_t slot = wave + NW * k;
+#pragma unroll
+          for (int rr = 0; rr < NF; ++rr) {
+            const uint32_t m = 4u * (g & 1u) + rr;
+            if (m < M) part[(((par * kSlots8 + slot) * 2u + h) * MMAX + m) * kRows + rw] = acc[k][rr];
+          }
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < NACC; ++k) acc[k] = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
+      __syncthreads();
+      if (tid < M * (uint32_t)kRows) {
+        const uint32_t m = tid >> 3, col = tid & 7u;
+        const uint32_t n = row + col;
+        if (n < N) {
+          const float *pp = part + (par * kSlots8 * 2u * MMAX + m) * kRows + col;
+          float v = pp[0];
+          for (uint32_t k = 1; k < 2u * kSlots8; ++k) v = v + pp[k * MMAX * kRows];
+          C[(size_t)m * N + n] = f32_to_bf16_rne(v);
+        }
+      }
+      // this parity's partials are next written after the following tile's barrier
+    }
+  };
+
+  while (cc.q + DEPTH <= nq) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) step(ring[d]);
+  }
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d)
+    if (cc.q < nq) step(ring[d]);
+}
+
+// Workgroups per compute unit allowed by registers (resolved once per kernel)
+// and by LDS (per call), times the compute units: a persistent grid.
+template <typename KernT>
+hipError_t resident_grid(KernT kern, int threads, size_t lds, uint32_t ntiles, uint32_t &grid) {
+  struct Res {
+    hipError_t err = hipSuccess;
+    int wg_per_cu = 1, cus = 1;
+  };
+  static const Res res = [kern, threads] {
+    Res r;
+    int dev = 0, per_cu = 0;
+    if ((r.err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax)) != hipSuccess)
+      return r;
+    if ((r.err = hipGetDevice(&dev)) != hipSuccess) return r;
+    if ((r.err = hipDeviceGetAttribute(&r.cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return r;
+    if ((r.err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, 0)) != hipSuccess) return r;
+    r.wg_per_cu = per_cu > 0 ? per_cu : 1;
+    if (r.cus < 1) r.cus = 1;
+    return r;
+  }();
+  if (res.err != hipSuccess) return res.err;
+  const int by_lds = (int)(kLdsMax / lds);
+  const int per_cu = by_lds < res.wg_per_cu ? (by_lds > 0 ? by_lds : 1) : res.wg_per_cu;
+  const uint32_t resident = (uint32_t)(per_cu * res.cus);
+  grid = ntiles < resident ? ntiles : resident;
+  return hipSuccess;
+}
+
+template <int MMAX>
 hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32_t K, uint32_t M,
                        hipStream_t stream) {
-  // Persistent grid: as many workgroups as fit on the device at once, each
-  // walking every gridDim.x-th tile.  Resolved once per process.
-  static int resident = 0;
-  if (resident == 0) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&(q2_0_mfma_kernel<MMAX, DEPTH>)),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, Layout<MMAX>::kTotal);
-    if (e != hipSuccess) return e;
-    int dev = 0, cus = 0, per_cu = 0;
-    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
-    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (q2_0_mfma_kernel<MMAX, DEPTH>), kThreads,
-                                                          Layout<MMAX>::kTotal)) != hipSuccess)
-      return e;
-    resident = (per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
+  const uint32_t ntiles = N >= (uint32_t)kRows ? (N + kRows - 1) / kRows : 1u;
+  const auto *a = static_cast<const uint16_t *>(A);
+  const auto *b = static_cast<const uint8_t *>(B);
+  auto *c = static_cast<uint16_t *>(C);
+  uint32_t grid = 0;
+  hipError_t e;
+  constexpr int NW = 8;
+  const size_t lds = pair_lds_bytes<MMAX>(M, K);
+  const bool bounded = (uint64_t)N * (K >> 7) * kBlockBytes < (1ull << 32);  // buffer-load range
+  if (lds <= kLdsMax && bounded) {  // activations fit in LDS: the pairs kernel
+    constexpr auto kern = q2_0_pairs_kernel<MMAX, NW, 2>;
+    if ((e = resident_grid(kern, 64 * NW, lds, ntiles, grid)) != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * NW), lds, stream, a, b, c, N, K, M);
+  } else {  // else per phase (same bits)
+    constexpr auto kern = q2_0_phase_kernel<MMAX, 2>;
+    const size_t plds = PhaseLayout<MMAX>::kFixed;
+    if ((e = resident_grid(kern, kThreads, plds, ntiles, grid)) != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), plds, stream, a, b, c, N, K, M);
   }
-  const uint32_t ntiles = (N + 15) / 16;
-  const uint32_t grid = ntiles < (uint32_t)resident ? ntiles : (uint32_t)resident;
-  hipLaunchKernelGGL((q2_0_mfma_kernel<MMAX, DEPTH>), dim3(grid), dim3(kThreads), Layout<MMAX>::kTotal, stream,
-                     static_cast<const uint16_t *>(A), static_cast<const uint8_t *>(B),
-                     static_cast<uint16_t *>(C), N, K, M);
   return hipGetLastError();
 }
 
 }  // namespace
 
-bool q2_0_mfma_supports(uint32_t K, uint32_t m) { return ((K >> 7) % 8u) == 0 && m >= 1 && m <= 16; }
+bool q2_0_mfma_supports(uint32_t K, uint32_t m) { return K >= 1024u && ((K >> 7) % 8u) == 0 && m >= 1 && m <= 8; }
 
 hipError_t launch_q2_0_mfma(const void *A, const void *B, void *C, uint32_t N, uint32_t K, uint32_t m,
                             hipStream_t stream) {
-  if (m <= 2) return launch_mmax<2, 2>(A, B, C, N, K, m, stream);
-  if (m <= 4) return launch_mmax<4, 2>(A, B, C, N, K, m, stream);
-  if (m <= 8) return launch_mmax<8, 2>(A, B, C, N, K, m, stream);
-  return launch_mmax<16, 2>(A, B, C, N, K, m, stream);
+  if (m <= 1) return launch_mmax<1>(A, B, C, N, K, m, stream);
+  if (m <= 2) return launch_mmax<2>(A, B, C, N, K, m, stream);
+  if (m <= 4) return launch_mmax<4>(A, B, C, N, K, m, stream);
+  return launch_mmax<8>(A, B, C, N, K, m, stream);
 }
 
 }  // namespace wqd
