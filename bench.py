@@ -179,20 +179,52 @@ def sweep_list():
 
 
 # ------------------------------------------------------------------- timing
+def graph_group(steps: int) -> int:
+    """Steps per captured graph: the largest divisor of `steps` up to 128, so
+    that exactly `steps` steps run in the timed region."""
+    return max(d for d in range(1, min(steps, 128) + 1) if steps % d == 0)
+
+
 def time_workload(torch, wqd, wl, steps, warmup):
-    """Time per step over the timed region: HIP events recorded on the stream
-    the kernels run on, around `steps` back-to-back steps."""
-    stream = torch.cuda.current_stream()
+    """Milliseconds per step over the timed region, HIP events recorded on the
+    stream the kernels run on.
+
+    Returns (graph, eager).  graph: `steps` steps replayed from HIP graphs of
+    G = graph_group(steps) captured steps each (each step of a graph uses its
+    own ring copy), which is how a decode loop issues fixed-shape launches and
+    leaves only the GPU's own per-dispatch cost between kernels.  eager: the
+    same steps launched one by one from Python, which adds the host's launch
+    cost (several microseconds per call) whenever that exceeds the kernel."""
     for i in range(warmup):
         wl.call(wqd, i)
     torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record(stream)
     for i in range(steps):
         wl.call(wqd, warmup + i)
     t1.record(stream)
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / steps
+    eager = t0.elapsed_time(t1) / steps
+
+    G = graph_group(steps)
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for i in range(G):
+                wl.call(wqd, warmup + i)
+    torch.cuda.synchronize()
+    graph.replay()  # one untimed replay
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(steps // G):
+        graph.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    del graph
+    return t0.elapsed_time(t1) / steps, eager
 
 
 def cpu_threads() -> int:
@@ -251,14 +283,15 @@ def main():
         log(f"[bench] {name}: ring of {wl.R} copies x {wl.bytes} B set up in {time.time() - t:.1f}s")
         wl.check(torch, np, oracle, lambda g, r: check_parity(g, r, name), 0)
         wl.check(torch, np, oracle, lambda g, r: check_parity(g, r, name), wl.R // 2 + 1)
-        step_ms = time_workload(torch, wqd, wl, steps, warmup)
+        step_ms, eager_ms = time_workload(torch, wqd, wl, steps, warmup)
         res = {"workload": name, "format": wl.fmt, "N": N, "K": K, "M": M, "ring": wl.R,
                "dispatches": wl.dispatches, "bytes_per_call": wl.bytes,
                "us_per_call": round(step_ms * 1e3, 3),
-               "gbs": round(wl.bytes / (step_ms * 1e-3) / 1e9, 1)}
+               "gbs": round(wl.bytes / (step_ms * 1e-3) / 1e9, 1),
+               "us_per_call_eager": round(eager_ms * 1e3, 3)}
         res["frac_hbm"] = round(res["gbs"] / HBM_PEAK_GBS, 4)
         log(f"[bench] {name}: {res['us_per_call']} us/call, {res['gbs']} GB/s, "
-            f"{100 * res['frac_hbm']:.1f}% of HBM peak")
+            f"{100 * res['frac_hbm']:.1f}% of HBM peak (eager launches: {res['us_per_call_eager']} us/call)")
         return wl, res
 
     if args.copy_probe:
@@ -310,7 +343,7 @@ def main():
             sweep.append(r2)
 
     kern_src = os.path.join(ROOT, "weight_quantized_decode_block_amd", "csrc", "q2_0_mfma.hip")
-    achieved = head["gbs"]  # one dispatch per step, back to back: step time = kernel duration
+    achieved = head["gbs"]  # one dispatch per step, back to back: step time = launch duration
     line = {
         "metric": METRIC,
         "value": head["gbs"],
@@ -326,13 +359,14 @@ def main():
         "data": "synthetic",
         "config": {"workload": "Q2_0 ternary GEMV M=1 N=5120 K=5120 group=128, bf16 activations, "
                                f"weights cold-cycled through {head['ring']} distinct copies "
-                               f"({head['ring'] * head['bytes_per_call'] / 2**20:.0f} MiB)",
+                               f"({head['ring'] * head['bytes_per_call'] / 2**20:.0f} MiB), "
+                               f"launches replayed from HIP graphs of {graph_group(args.steps)} steps",
                    "bytes_per_call": head["bytes_per_call"], "frac_hbm_peak": head["frac_hbm"],
-                   "us_per_call": head["us_per_call"]},
+                   "us_per_call": head["us_per_call"], "us_per_call_eager": head["us_per_call_eager"]},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profile(kern_src, "q2_0_gemv_kernel_m1_5120x5120"),
-                     "kernel": "q2_0_mfma_kernel<2>", "kernel_us_avg": head["us_per_call"]},
+                     "kernel": "q2_0_pairs_kernel<1, 8, 2>", "kernel_us_avg": head["us_per_call"]},
         "cpu_baseline": cpu,
     }
     if sweep:

@@ -80,10 +80,20 @@ def _ptr(x) -> int | None:
     return int(x.data_ptr())
 
 
+_current_raw_stream = None
+
+
 def _stream(stream) -> int | None:
+    global _current_raw_stream
     if stream is None:
-        import torch
-        return int(torch.cuda.current_stream().cuda_stream)
+        if _current_raw_stream is None:
+            import torch
+            raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+            if raw is not None:
+                _current_raw_stream = lambda: raw(torch.cuda.current_device())
+            else:
+                _current_raw_stream = lambda: int(torch.cuda.current_stream().cuda_stream)
+        return _current_raw_stream()
     if isinstance(stream, int):
         return stream
     return int(stream.cuda_stream)
