@@ -371,7 +371,7 @@ struct PairRegs {
 // Weight bytes go straight from memory to the lanes that use them (buffer
 // loads bounded by the matrix size): lane (h, r, g) reads 12 bytes at
 // 68p + 32h + 8g of weight row r and 2 bytes (the scale) at 68p + 34h.
-template <int MMAX, int NW, int DEPTH>
+template <int MMAX, int NW, int DEPTH, int UA>
 __global__ __launch_bounds__(64 * NW) void q2_0_pairs_kernel(const uint16_t *__restrict__ A,
                                                              const uint8_t *__restrict__ B,
                                                              uint16_t *__restrict__ C, uint32_t N, uint32_t K,
@@ -452,10 +452,12 @@ __global__ __launch_bounds__(64 * NW) void q2_0_pairs_kernel(const uint16_t *__r
   // ---- prologue: A into LDS (permuted) while the first DEPTH pairs are in flight
   PairRegs ring[DEPTH];
   {
-    constexpr int U = 1024 / (64 * NW);  // chunks per thread per round (1024 per workgroup)
+    // UA chunks per thread per round: the launcher picks UA so that one round
+    // usually holds all of A; later rounds wait behind the ring's loads
     const uint32_t cpr = K >> 3;
     const uint32_t total = M * cpr;
     const uint32_t spare = tid % total;  // in-bounds chunk re-read by idle slots
+    constexpr int U = UA;
     u32x4_t av[U];
     uint32_t adst[U];
     auto a_load = [&](uint32_t base) {
@@ -571,23 +573,25 @@ __global__ __launch_bounds__(64 * NW) void q2_0_pairs_kernel(const uint16_t *__r
     if (cc.q < nq) step(ring[d]);
 }
 
-// Workgroups per compute unit allowed by registers (resolved once per kernel)
-// and by LDS (per call), times the compute units: a persistent grid.
-template <typename KernT>
-hipError_t resident_grid(KernT kern, int threads, size_t lds, uint32_t ntiles, uint32_t &grid) {
+// Launches KERN as a persistent grid: as many workgroups as fit on the device
+// at once, by registers (resolved once per kernel and process) and by LDS
+// (per call), each walking every gridDim.x-th tile.
+template <auto KERN>
+hipError_t launch_persistent(int threads, size_t lds, uint32_t ntiles, hipStream_t stream, const uint16_t *a,
+                             const uint8_t *b, uint16_t *c, uint32_t N, uint32_t K, uint32_t M) {
   struct Res {
     hipError_t err = hipSuccess;
     int wg_per_cu = 1, cus = 1;
   };
-  static const Res res = [kern, threads] {
+  static const Res res = [threads] {
     Res r;
     int dev = 0, per_cu = 0;
-    if ((r.err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+    if ((r.err = hipFuncSetAttribute(reinterpret_cast<const void *>(KERN),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax)) != hipSuccess)
       return r;
     if ((r.err = hipGetDevice(&dev)) != hipSuccess) return r;
     if ((r.err = hipDeviceGetAttribute(&r.cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return r;
-    if ((r.err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, 0)) != hipSuccess) return r;
+    if ((r.err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, KERN, threads, 0)) != hipSuccess) return r;
     r.wg_per_cu = per_cu > 0 ? per_cu : 1;
     if (r.cus < 1) r.cus = 1;
     return r;
@@ -596,8 +600,9 @@ hipError_t resident_grid(KernT kern, int threads, size_t lds, uint32_t ntiles, u
   const int by_lds = (int)(kLdsMax / lds);
   const int per_cu = by_lds < res.wg_per_cu ? (by_lds > 0 ? by_lds : 1) : res.wg_per_cu;
   const uint32_t resident = (uint32_t)(per_cu * res.cus);
-  grid = ntiles < resident ? ntiles : resident;
-  return hipSuccess;
+  const uint32_t grid = ntiles < resident ? ntiles : resident;
+  hipLaunchKernelGGL(KERN, dim3(grid), dim3(threads), lds, stream, a, b, c, N, K, M);
+  return hipGetLastError();
 }
 
 template <int MMAX>
@@ -607,22 +612,21 @@ hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32
   const auto *a = static_cast<const uint16_t *>(A);
   const auto *b = static_cast<const uint8_t *>(B);
   auto *c = static_cast<uint16_t *>(C);
-  uint32_t grid = 0;
-  hipError_t e;
   constexpr int NW = 8;
   const size_t lds = pair_lds_bytes<MMAX>(M, K);
   const bool bounded = (uint64_t)N * (K >> 7) * kBlockBytes < (1ull << 32);  // buffer-load range
   if (lds <= kLdsMax && bounded) {  // activations fit in LDS: the pairs kernel
-    constexpr auto kern = q2_0_pairs_kernel<MMAX, NW, 2>;
-    if ((e = resident_grid(kern, 64 * NW, lds, ntiles, grid)) != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * NW), lds, stream, a, b, c, N, K, M);
-  } else {  // else per phase (same bits)
-    constexpr auto kern = q2_0_phase_kernel<MMAX, 2>;
-    const size_t plds = PhaseLayout<MMAX>::kFixed;
-    if ((e = resident_grid(kern, kThreads, plds, ntiles, grid)) != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), plds, stream, a, b, c, N, K, M);
+    // activation chunks per thread for one staging round covering all of A
+    const uint32_t per_thread = (M * (K >> 3) + 64 * NW - 1) / (64 * NW);
+    if (per_thread <= 2)
+      return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 2>>(64 * NW, lds, ntiles, stream, a, b, c, N, K, M);
+    if (per_thread <= 4)
+      return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 4>>(64 * NW, lds, ntiles, stream, a, b, c, N, K, M);
+    return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 10>>(64 * NW, lds, ntiles, stream, a, b, c, N, K, M);
   }
-  return hipGetLastError();
+  // else per phase (same bits)
+  return launch_persistent<q2_0_phase_kernel<MMAX, 2>>(kThreads, PhaseLayout<MMAX>::kFixed, ntiles, stream, a, b, c,
+                                                       N, K, M);
 }
 
 }  // namespace
