@@ -236,10 +236,246 @@ hipError_t launch_slots(const void *A, const void *W, const float *S, void *C, u
   return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------------------
+// Resident-activation kernel (the usual decode case, when all M rows of A fit
+// in LDS): same arithmetic, block order and reduction order as the kernel
+// above, so both give the same bits.  Weight bytes go straight from memory to
+// the lanes that use them, and each wave works on its own blocks without
+// waiting for the others until the end of a tile.
+//   * A workgroup of 8 waves walks its tiles of 16 weight rows (blockIdx.x,
+//     + gridDim.x, ...); wave w owns blocks w, w + 8, ... of every tile.
+//   * Per block, lane (i, g) loads the 32 weights k = 32g..32g+31 of row
+//     n0 + i (two 16-byte buffer loads, bounded by the matrix size; rows past
+//     N re-read row N - 1) and the block's scale (a uniform 4-byte load),
+//     DEPTH blocks ahead of the compute.
+//   * Activations are copied into LDS once per workgroup; lane (i, g) reads
+//     its 64 bytes of row i (rows i >= M read row 0 and feed outputs that are
+//     never stored).
+//   * At the end of a tile the 8 waves' accumulators are added in LDS in wave
+//     order and rows m < M are stored.
+// ---------------------------------------------------------------------------
+struct UnitRegs {
+  u32x4_t w0, w1;  // this lane's 32 FP8 weights of the block
+  float s;         // the block's scale
+};
+
+template <int MMAX>
+struct UnitLayout {
+  static constexpr int kPart = 0;  // [tile parity][wave][m][16] floats
+  static constexpr int kA = kPart + 2 * kWaves * MMAX * 16 * 4;
+};
+
+template <int MMAX>
+constexpr size_t unit_lds_bytes(uint32_t M, uint32_t K) {
+  return (size_t)UnitLayout<MMAX>::kA + (size_t)M * (2u * K + 16u);
+}
+
+template <int MMAX, int DEPTH, int UA>
+__global__ __launch_bounds__(kThreads) void w8a16_units_kernel(const uint16_t *__restrict__ A,
+                                                               const uint8_t *__restrict__ W,
+                                                               const float *__restrict__ S,
+                                                               uint16_t *__restrict__ C, uint32_t M, uint32_t N,
+                                                               uint32_t K) {
+  using L = UnitLayout<MMAX>;
+  constexpr int NF = MMAX < 4 ? MMAX : 4;  // accumulator rows that can hold outputs
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const uint32_t tid = threadIdx.x;
+  const uint32_t lane = tid & 63u;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t i = lane & 15u, g = lane >> 4;
+  const uint32_t nb = K >> 7;
+  const uint32_t ntiles = (N + 15u) >> 4;
+  const uint32_t my_tiles = (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x;
+  // blocks of a tile owned by this wave: wave, wave + 8, ...; a wave that
+  // owns none (K < 1024) runs one empty unit per tile to meet the barrier
+  const uint32_t upw = nb > wave ? (nb - wave + kWaves - 1) / kWaves : 1u;
+  const uint32_t nq = my_tiles * upw;
+  const uint32_t a_pitch = 2u * K + 16u;
+
+  const __amdgpu_buffer_rsrc_t wrsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(W), (short)0, (int)(N * K), 0x00020000);
+  const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float *>(S), (short)0, (int)(((N + 127u) >> 7) * nb * 4u), 0x00020000);
+
+  struct Cursor {
+    uint32_t q, u, j, n0;  // unit, block index within the tile's share, tile index, tile's first row
+  };
+  const uint32_t n0_step = 16u * gridDim.x;
+  auto advance = [&](Cursor &c) {
+    ++c.q;
+    if (++c.u == upw) {
+      c.u = 0;
+      ++c.j;
+      c.n0 += n0_step;
+    }
+  };
+  Cursor ld = {0u, 0u, 0u, 16u * blockIdx.x};
+  const uint32_t w_lane = 32u * g;
+  auto issue_next = [&]() {
+    const bool live = ld.q < nq;
+    const uint32_t b = min(wave + kWaves * ld.u, nb - 1u);
+    const uint32_t n0 = live ? ld.n0 : 16u * blockIdx.x;
+    const uint32_t row = min(n0 + i, N - 1u);
+    const uint32_t voff = row * K + w_lane;
+    const uint32_t soff = 128u * b;
+    UnitRegs r;
+    r.w0 = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, voff, soff, 0);
+    r.w1 = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, voff + 16u, soff, 0);
+    r.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srsrc, 0u, ((n0 >> 7) * nb + b) * 4u, 0));
+    advance(ld);
+    return r;
+  };
+
+  const uint32_t a_lane = (i < M ? i : 0u) * a_pitch + 64u * g;  // + L::kA + 256 per block
+  float *part = reinterpret_cast<float *>(lds + L::kPart);
+
+  UnitRegs ring[DEPTH];
+  {  // A into LDS while the first DEPTH blocks are in flight
+    const uint32_t cpr = K >> 3;
+    const uint32_t total = M * cpr;
+    const uint32_t spare = tid % total;
+    u32x4_t av[UA];
+    uint32_t adst[UA];
+    auto a_load = [&](uint32_t base) {
+#pragma unroll
+      for (int u = 0; u < UA; ++u) {
+        const uint32_t c = base + (uint32_t)u * kThreads + tid;
+        const bool in = c < total;
+        const uint32_t cc = in ? c : spare;
+        const uint32_t m = cc / cpr, col = cc - m * cpr;
+        av[u] = *reinterpret_cast<const u32x4_t *>(reinterpret_cast<const uint8_t *>(A) + (size_t)cc * 16u);
+        adst[u] = in ? L::kA + m * a_pitch + 16u * col : (uint32_t)L::kPart;  // idle: into the partials
+      }
+    };
+    auto a_store = [&]() {
+#pragma unroll
+      for (int u = 0; u < UA; ++u) *reinterpret_cast<u32x4_t *>(lds + adst[u]) = av[u];
+    };
+    a_load(0u);
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) ring[d] = issue_next();
+    a_store();
+    for (uint32_t base = UA * kThreads; base < total; base += UA * kThreads) {
+      a_load(base);
+      a_store();
+    }
+    __syncthreads();
+  }
+
+  f32x4_t outer = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto unit = [&](const UnitRegs &r, uint32_t b) {
+    const uint8_t *act = lds + L::kA + a_lane + 256u * b;
+    bf16x8_t a[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = *reinterpret_cast<const bf16x8_t *>(act + 16 * j);
+    f32x4_t x = {0.0f, 0.0f, 0.0f, 0.0f};
+    x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], weights8(r.w0.x, r.w0.y), x, 0, 0, 0);
+    x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], weights8(r.w0.z, r.w0.w), x, 0, 0, 0);
+    x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2], weights8(r.w1.x, r.w1.y), x, 0, 0, 0);
+    x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[3], weights8(r.w1.z, r.w1.w), x, 0, 0, 0);
+#pragma unroll
+    for (int rr = 0; rr < NF; ++rr) outer[rr] = __fadd_rn(outer[rr], __fmul_rn(r.s, x[rr]));
+  };
+
+  Cursor cc = {0u, 0u, 0u, 16u * blockIdx.x};
+  auto step = [&](UnitRegs &r) {
+    const uint32_t j = cc.j, u = cc.u, n0 = cc.n0;
+    const uint32_t b = wave + kWaves * u;
+    if (b < nb) unit(r, b);
+    r = issue_next();
+    advance(cc);
+    if (u + 1u == upw) {  // tile done: add the 8 waves' partial tiles in wave order
+      const uint32_t par = j & 1u;
+#pragma unroll
+      for (int rr = 0; rr < NF; ++rr) {
+        const uint32_t m = 4u * g + rr;
+        if (m < M) part[((par * kWaves + wave) * MMAX + m) * 16u + i] = outer[rr];
+      }
+      outer = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
+      __syncthreads();
+      if (tid < M * 16u) {
+        const uint32_t m = tid >> 4, col = tid & 15u;
+        const uint32_t n = n0 + col;
+        if (n < N) {
+          const float *pp = part + (par * kWaves * MMAX + m) * 16u + col;
+          float v = pp[0];
+          for (uint32_t w = 1; w < kWaves; ++w) v = v + pp[w * MMAX * 16u];
+          C[(size_t)m * N + n] = f32_to_bf16_rne(v);
+        }
+      }
+      // this parity's partials are next written after the following tile's barrier
+    }
+  };
+
+  while (cc.q + DEPTH <= nq) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) step(ring[d]);
+  }
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d)
+    if (cc.q < nq) step(ring[d]);
+}
+
+// Launches KERN as a persistent grid: as many workgroups as fit on the device
+// at once, by registers (resolved once per kernel and process) and by LDS
+// (per call), each walking every gridDim.x-th tile.
+template <auto KERN>
+hipError_t launch_units(size_t lds, uint32_t ntiles, hipStream_t stream, const uint16_t *a, const uint8_t *w,
+                        const float *s, uint16_t *c, uint32_t M, uint32_t N, uint32_t K) {
+  struct Res {
+    hipError_t err = hipSuccess;
+    int wg_per_cu = 1, cus = 1;
+  };
+  static const Res res = [] {
+    Res r;
+    int dev = 0, per_cu = 0;
+    if ((r.err = hipFuncSetAttribute(reinterpret_cast<const void *>(KERN),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024)) != hipSuccess)
+      return r;
+    if ((r.err = hipGetDevice(&dev)) != hipSuccess) return r;
+    if ((r.err = hipDeviceGetAttribute(&r.cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return r;
+    if ((r.err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, KERN, kThreads, 0)) != hipSuccess) return r;
+    r.wg_per_cu = per_cu > 0 ? per_cu : 1;
+    if (r.cus < 1) r.cus = 1;
+    return r;
+  }();
+  if (res.err != hipSuccess) return res.err;
+  const int by_lds = (int)((160u * 1024u) / lds);
+  const int per_cu = by_lds < res.wg_per_cu ? (by_lds > 0 ? by_lds : 1) : res.wg_per_cu;
+  const uint32_t resident = (uint32_t)(per_cu * res.cus);
+  const uint32_t grid = ntiles < resident ? ntiles : resident;
+  hipLaunchKernelGGL(KERN, dim3(grid), dim3(kThreads), lds, stream, a, w, s, c, M, N, K);
+  return hipGetLastError();
+}
+
+template <int MMAX>
+hipError_t launch_units_mmax(const void *A, const void *W, const float *S, void *C, uint32_t M, uint32_t N,
+                             uint32_t K, hipStream_t stream) {
+  const size_t lds = unit_lds_bytes<MMAX>(M, K);
+  const uint32_t ntiles = (N + 15u) / 16u;
+  const auto *a = static_cast<const uint16_t *>(A);
+  const auto *w = static_cast<const uint8_t *>(W);
+  auto *c = static_cast<uint16_t *>(C);
+  const uint32_t per_thread = (M * (K >> 3) + kThreads - 1) / kThreads;
+  if (per_thread <= 2) return launch_units<w8a16_units_kernel<MMAX, 2, 2>>(lds, ntiles, stream, a, w, S, c, M, N, K);
+  if (per_thread <= 4) return launch_units<w8a16_units_kernel<MMAX, 2, 4>>(lds, ntiles, stream, a, w, S, c, M, N, K);
+  return launch_units<w8a16_units_kernel<MMAX, 2, 10>>(lds, ntiles, stream, a, w, S, c, M, N, K);
+}
+
 }  // namespace
 
 hipError_t launch_w8a16_m16(const void *A, const void *W, const float *S, void *C, uint32_t M, uint32_t N,
                             uint32_t K, hipStream_t stream) {
+  // the resident-activation kernel when A fits in LDS and the weights in one
+  // buffer range; the per-phase kernel otherwise (same bits either way)
+  const bool bounded = (uint64_t)N * K < (1ull << 31);
+  if (bounded && M <= 8 && unit_lds_bytes<8>(M, K) <= 160u * 1024u) {
+    if (M <= 1) return launch_units_mmax<1>(A, W, S, C, M, N, K, stream);
+    if (M <= 2) return launch_units_mmax<2>(A, W, S, C, M, N, K, stream);
+    if (M <= 4) return launch_units_mmax<4>(A, W, S, C, M, N, K, stream);
+    return launch_units_mmax<8>(A, W, S, C, M, N, K, stream);
+  }
   if (M <= 4) return launch_slots<slots_for(4)>(A, W, S, C, M, N, K, stream);
   if (M <= 8) return launch_slots<slots_for(8)>(A, W, S, C, M, N, K, stream);
   return launch_slots<slots_for(16)>(A, W, S, C, M, N, K, stream);
