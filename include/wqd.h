@@ -123,6 +123,43 @@ int q2_0_gemv_batchm(const void *A, const void *B, void *C,
 int w8a16_gemm_m16(const void *A, const void *W, const float *S, void *C,
                    uint32_t M, uint32_t N, uint32_t K, hipStream_t stream);
 
+/*
+ * w8a16_gemm_m16_n64 - the same GEMM with each workgroup owning 64
+ * consecutive weight rows (four 16-row tiles) instead of spreading tiles over
+ * the matrix: a quarter as many workgroups as there are 16-row tiles.
+ * Defined by page "w8a16_gemm_m16.rs", docs of W8A16_GEMM_M16_N_TILE_WIDE and
+ * w8a16_gemm_m16_n64 (same arguments and guards as w8a16_gemm_m16, wider N
+ * tile, fewer workgroups).  Arguments, checks and error codes are those of
+ * w8a16_gemm_m16; the output is bit-identical to it (same sums, same order).
+ */
+int w8a16_gemm_m16_n64(const void *A, const void *W, const float *S, void *C,
+                       uint32_t M, uint32_t N, uint32_t K, hipStream_t stream);
+
+/*
+ * w8a16_gemm_m16_strided - w8a16_gemm_m16 with row pitches for A and C, so
+ * the rows may be slices of wider row-major buffers.
+ * Defined by page "w8a16_gemm_m16.rs", doc of w8a16_gemm_m16_strided (pitches
+ * in elements, each covering its row, the activation pitch a multiple of 8 so
+ * every row starts on a 16-byte boundary).
+ *
+ *   A             device, BF16, row m at A + m * a_row_stride, 16-byte aligned
+ *   C             device, BF16, row m at C + m * c_row_stride, 2-byte aligned;
+ *                 only elements [0, N) of rows < M are written, the padding
+ *                 between rows is never touched
+ *   a_row_stride  >= K and a multiple of 8 (else WQD_EINVAL)
+ *   c_row_stride  >= N (else WQD_EINVAL)
+ *   W, S, M, N, K as for w8a16_gemm_m16; (M-1)*pitch + row must stay below
+ *   2^32 elements for both A and C (else WQD_EINVAL)
+ *
+ * With a_row_stride = K and c_row_stride = N it is w8a16_gemm_m16, bit for
+ * bit; in general each output row is bit-identical to w8a16_gemm_m16 on the
+ * same row stored contiguously.
+ */
+int w8a16_gemm_m16_strided(const void *A, const void *W, const float *S, void *C,
+                           uint32_t M, uint32_t N, uint32_t K,
+                           uint32_t a_row_stride, uint32_t c_row_stride,
+                           hipStream_t stream);
+
 /* ----------------------------------------------------------- host helpers */
 
 /* Bytes of a packed Q2_0 matrix: N * (K/128) * 34, or 0 if K % 128 != 0. */

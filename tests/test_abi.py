@@ -28,8 +28,9 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = wqd.header_functions()
-    assert set(names) >= {"q2_0_gemv", "q2_0_gemv_batchm", "w8a16_gemm_m16", "q2_0_packed_bytes",
-                          "q2_0_pack", "q2_0_batchm_chunks", "wqd_last_error"}
+    assert set(names) >= {"q2_0_gemv", "q2_0_gemv_batchm", "w8a16_gemm_m16", "w8a16_gemm_m16_n64",
+                          "w8a16_gemm_m16_strided", "q2_0_packed_bytes", "q2_0_pack",
+                          "q2_0_batchm_chunks", "wqd_last_error"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -74,10 +75,43 @@ def test_q2_0_batchm_validation(L):
     ((FAKE, FAKE + 4, FAKE, FAKE, 16, 64, 1024), wqd.WQD_EALIGN, "W must"),
     ((FAKE, FAKE, FAKE + 2, FAKE, 16, 64, 1024), wqd.WQD_EALIGN, "S must"),
 ])
-def test_w8a16_validation(L, args, code, frag):
-    rc = L.w8a16_gemm_m16(*args, None)
+@pytest.mark.parametrize("fn", ["w8a16_gemm_m16", "w8a16_gemm_m16_n64", "w8a16_gemm_m16_strided"])
+def test_w8a16_validation(L, fn, args, code, frag):
+    """The three W8A16 entry points share the guards of page "w8a16_gemm_m16.rs"."""
+    extra = (args[6], args[5]) if fn.endswith("_strided") else ()  # pitches = K, N
+    rc = getattr(L, fn)(*args, *extra, None)
     assert rc == code
     assert frag in wqd.last_error()
+    assert fn in wqd.last_error()
+
+
+@pytest.mark.parametrize("M,N,K,lda,ldc,frag", [
+    (4, 64, 1024, 1016, 64, "cover"),      # a_row_stride < K
+    (4, 64, 1024, 1024, 63, "cover"),      # c_row_stride < N
+    (4, 64, 1024, 1028, 64, "multiple of 8"),
+    (4, 64, 1024, 1030, 70, "multiple of 8"),
+    (16, 64, 1024, 0x12000000, 64, "too large"),   # 15 * pitch + K >= 2^32
+    (16, 64, 1024, 1024, 0x12000000, "too large"),
+])
+def test_w8a16_strided_validation(L, M, N, K, lda, ldc, frag):
+    """Pitch rules of page "w8a16_gemm_m16.rs" (doc of w8a16_gemm_m16_strided)."""
+    rc = L.w8a16_gemm_m16_strided(FAKE, FAKE, FAKE, FAKE, M, N, K, lda, ldc, None)
+    assert rc == wqd.WQD_EINVAL
+    assert frag in wqd.last_error()
+
+
+@pytest.mark.parametrize("lda,ldc", [(1024, 64), (1032, 65), (4096, 1000)])
+def test_w8a16_strided_valid_pitches_reach_the_device_check(L, lda, ldc):
+    """Pitches that meet the rules pass validation (no GPU here, so the call
+    stops at the device check)."""
+    try:
+        import torch
+        if torch.cuda.is_available():
+            pytest.skip("a GPU is present")
+    except ImportError:
+        pass
+    rc = L.w8a16_gemm_m16_strided(FAKE, FAKE, FAKE, FAKE, 4, 64, 1024, lda, ldc, None)
+    assert rc in (wqd.WQD_ENODEV, wqd.WQD_EHIP)
 
 
 def test_valid_call_without_gpu_reports_no_device(L):

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 import torch
 
-from parity import CANARY, check_parity, dev_f32, dev_u8, requires_gpu, ulp_histogram, w8a16_gpu
+from parity import CANARY, check_parity, dev_f32, dev_u8, dev_u16, host_u16, requires_gpu, ulp_histogram, w8a16_gpu
 from weight_quantized_decode_block_amd import inputs as gen
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
@@ -93,3 +93,77 @@ def test_ffn_shapes(oracle_mod, N, K):
     cols = np.sort(gen.rng(906, N, K).choice(N, 384, replace=False))
     ref = np.concatenate([oracle_mod.w8a16_gemm(A[16:], W[c:c + 1], S[c // 128:c // 128 + 1]) for c in cols], axis=1)
     check_parity(got32[16:, cols], ref, f"w8a16 {N}x{K} rows 16..31 sampled")
+
+
+# --------------------------------------------- _n64 and _strided variants
+def _contiguous(A, Wd, Sd, N, K):
+    return w8a16_gpu(A, Wd, Sd, N, K)
+
+
+@pytest.mark.parametrize("N,K,M", [(5120, 5120, 1), (5120, 5120, 8), (5120, 5120, 16), (17, 384, 3),
+                                   (130, 1152, 12), (200, 256, 9), (4095, 640, 2), (1, 128, 1), (80, 1024, 5)])
+def test_n64_bit_identical_to_contiguous(oracle_mod, N, K, M):
+    """64-row bands per workgroup (page "w8a16_gemm_m16.rs", w8a16_gemm_m16_n64):
+    same sums in the same order, so every output equals w8a16_gemm_m16's; rows
+    >= M stay untouched."""
+    from weight_quantized_decode_block_amd import wqd
+    A, W, S = _case(21, N, K, M, salt=N + 3 * K)
+    Wd, Sd = dev_u8(W), dev_f32(S)
+    ref = _contiguous(A, Wd, Sd, N, K)
+    C = torch.full((16, N), CANARY, dtype=torch.int16, device="cuda")
+    wqd.w8a16_gemm_m16_n64(dev_u16(A), Wd, Sd, C, M, N, K)
+    torch.cuda.synchronize()
+    got = host_u16(C)
+    assert np.array_equal(got[:M], ref)
+    assert np.all(got[M:] == CANARY)
+    if N * K <= 1 << 20:
+        check_parity(got[:M], oracle_mod.w8a16_gemm(A, W, S), f"w8a16 n64 N={N} K={K} M={M}")
+
+
+@pytest.mark.parametrize("N,K,M,pa,pc", [
+    (5120, 5120, 1, 0, 0), (5120, 5120, 8, 8, 1), (5120, 5120, 16, 136, 37),
+    (130, 1024, 16, 8, 3), (17, 384, 3, 64, 0), (300, 640, 7, 0, 300), (33, 128, 9, 1024, 5),
+])
+def test_strided_rows_equal_contiguous_and_padding_untouched(oracle_mod, N, K, M, pa, pc):
+    """A and C as row slices of wider buffers (page "w8a16_gemm_m16.rs",
+    w8a16_gemm_m16_strided): each output row equals the contiguous call's, the
+    activation padding (filled with NaN bit patterns) is never read into a
+    sum, and C's padding columns and rows >= M keep their canary."""
+    from weight_quantized_decode_block_amd import wqd
+    A, W, S = _case(22, N, K, M, salt=N + 5 * K)
+    Wd, Sd = dev_u8(W), dev_f32(S)
+    ref = _contiguous(A, Wd, Sd, N, K)
+    lda, ldc = K + pa, N + pc
+    Ab = np.full((M, lda), 0x7FC1, np.uint16)  # NaN padding: a stray read would show in C
+    Ab[:, :K] = A
+    C = torch.full((M + 1, ldc), CANARY, dtype=torch.int16, device="cuda")
+    wqd.w8a16_gemm_m16_strided(dev_u16(Ab), Wd, Sd, C, M, N, K, lda, ldc)
+    torch.cuda.synchronize()
+    got = host_u16(C)
+    assert np.array_equal(got[:M, :N], ref)
+    assert np.all(got[:M, N:] == CANARY)
+    assert np.all(got[M:] == CANARY)
+    if N * K <= 1 << 20:
+        check_parity(got[:M, :N], oracle_mod.w8a16_gemm(A, W, S), f"w8a16 strided N={N} K={K} M={M}")
+
+
+def test_strided_slices_of_a_shared_buffer(oracle_mod):
+    """Two calls write column slices of one output buffer and read column
+    slices of one activation buffer (a multi-sequence buffer with Q, K and V
+    side by side): each slice equals its own contiguous call."""
+    from weight_quantized_decode_block_amd import wqd
+    M, K, N0, N1 = 6, 1024, 640, 384
+    A2 = gen.activations(23, 2 * K, M, 0)  # [M, 2K]: two activation sets side by side
+    W0, S0 = gen.w8a16_weights(24, N0, K, 0)
+    W1, S1 = gen.w8a16_weights(25, N1, K, 0)
+    Ad = dev_u16(A2)
+    C = torch.full((M, N0 + N1 + 8), CANARY, dtype=torch.int16, device="cuda")
+    wqd.w8a16_gemm_m16_strided(Ad, dev_u8(W0), dev_f32(S0), C, M, N0, K, 2 * K, N0 + N1 + 8)
+    wqd.w8a16_gemm_m16_strided(Ad[:, K:], dev_u8(W1), dev_f32(S1), C[:, N0:], M, N1, K, 2 * K, N0 + N1 + 8)
+    torch.cuda.synchronize()
+    got = host_u16(C)
+    assert np.array_equal(got[:, :N0], _contiguous(np.ascontiguousarray(A2[:, :K]), dev_u8(W0), dev_f32(S0), N0, K))
+    assert np.array_equal(got[:, N0:N0 + N1],
+                          _contiguous(np.ascontiguousarray(A2[:, K:]), dev_u8(W1), dev_f32(S1), N1, K))
+    assert np.all(got[:, N0 + N1:] == CANARY)
+    check_parity(got[:, :N0], oracle_mod.w8a16_gemm(np.ascontiguousarray(A2[:, :K]), W0, S0), "slice 0")

@@ -4,8 +4,8 @@
 //
 // Behaviour follows page "gemv_q2_vec.rs" (q2_0_gemv_vec launcher; the
 // batched launcher's Q2_BATCHM_MAX_M chunking, batchm_row_chunks and
-// batchm_launch_chunks) and page "w8a16_gemm_m16.rs" (w8a16_gemm_m16's checks
-// 1 <= m <= 16 and K % 128 == 0).
+// batchm_launch_chunks) and page "w8a16_gemm_m16.rs" (the checks of
+// w8a16_gemm_m16 and its _n64 and _strided variants).
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -95,6 +95,25 @@ int validate_q2_0(const char *fn, const void *A, const void *B, void *C, uint32_
   return WQD_OK;
 }
 
+// Checks shared by the three W8A16 entry points (page "w8a16_gemm_m16.rs":
+// 1 <= m <= 16, K a multiple of 128).
+int validate_w8a16(const char *fn, const void *A, const void *W, const float *S, void *C, uint32_t M,
+                   uint32_t N, uint32_t K) {
+  if (!A || !W || !S || !C) return fail(WQD_ENULL, "%s: A, W, S and C must be non-NULL", fn);
+  if (M < 1 || M > WQD_W8A16_MAX_M) return fail(WQD_EINVAL, "%s: m=%u outside 1..16 (the M tile)", fn, M);
+  if (K == 0 || K % WQD_W8A16_BLOCK != 0)
+    return fail(WQD_EINVAL, "%s: K=%u is not a positive multiple of 128 (block-scale granularity)", fn, K);
+  if (N == 0) return fail(WQD_EINVAL, "%s: N must be >= 1", fn);
+  if (!aligned(A, 16)) return fail(WQD_EALIGN, "%s: A must be 16-byte aligned", fn);
+  if (!aligned(W, 16)) return fail(WQD_EALIGN, "%s: W must be 16-byte aligned", fn);
+  if (!aligned(S, 4)) return fail(WQD_EALIGN, "%s: S must be 4-byte aligned", fn);
+  if (!aligned(C, 2)) return fail(WQD_EALIGN, "%s: C must be 2-byte aligned", fn);
+  return WQD_OK;
+}
+
+// 16-row tiles per workgroup in w8a16_gemm_m16_n64: 64 weight rows each.
+constexpr uint32_t kN64Band = 4;
+
 }  // namespace
 
 extern "C" {
@@ -151,19 +170,39 @@ int q2_0_gemv_batchm(const void *A, const void *B, void *C, uint32_t N, uint32_t
 int w8a16_gemm_m16(const void *A, const void *W, const float *S, void *C, uint32_t M, uint32_t N,
                    uint32_t K, hipStream_t stream) {
   static const char fn[] = "w8a16_gemm_m16";
-  if (!A || !W || !S || !C) return fail(WQD_ENULL, "%s: A, W, S and C must be non-NULL", fn);
-  if (M < 1 || M > WQD_W8A16_MAX_M) return fail(WQD_EINVAL, "%s: m=%u outside 1..16 (the M tile)", fn, M);
-  if (K == 0 || K % WQD_W8A16_BLOCK != 0)
-    return fail(WQD_EINVAL, "%s: K=%u is not a positive multiple of 128 (block-scale granularity)", fn, K);
-  if (N == 0) return fail(WQD_EINVAL, "%s: N must be >= 1", fn);
-  if (!aligned(A, 16)) return fail(WQD_EALIGN, "%s: A must be 16-byte aligned", fn);
-  if (!aligned(W, 16)) return fail(WQD_EALIGN, "%s: W must be 16-byte aligned", fn);
-  if (!aligned(S, 4)) return fail(WQD_EALIGN, "%s: S must be 4-byte aligned", fn);
-  if (!aligned(C, 2)) return fail(WQD_EALIGN, "%s: C must be 2-byte aligned", fn);
-  int rc = check_device(fn);
+  int rc = validate_w8a16(fn, A, W, S, C, M, N, K);
   if (rc) return rc;
+  if ((rc = check_device(fn))) return rc;
   (void)hipGetLastError();
-  return check_launch(fn, wqd::launch_w8a16_m16(A, W, S, C, M, N, K, stream));
+  return check_launch(fn, wqd::launch_w8a16_m16(A, W, S, C, M, N, K, K, N, 1, stream));
+}
+
+int w8a16_gemm_m16_n64(const void *A, const void *W, const float *S, void *C, uint32_t M, uint32_t N,
+                       uint32_t K, hipStream_t stream) {
+  static const char fn[] = "w8a16_gemm_m16_n64";
+  int rc = validate_w8a16(fn, A, W, S, C, M, N, K);
+  if (rc) return rc;
+  if ((rc = check_device(fn))) return rc;
+  (void)hipGetLastError();
+  return check_launch(fn, wqd::launch_w8a16_m16(A, W, S, C, M, N, K, K, N, kN64Band, stream));
+}
+
+int w8a16_gemm_m16_strided(const void *A, const void *W, const float *S, void *C, uint32_t M, uint32_t N,
+                           uint32_t K, uint32_t a_row_stride, uint32_t c_row_stride, hipStream_t stream) {
+  static const char fn[] = "w8a16_gemm_m16_strided";
+  int rc = validate_w8a16(fn, A, W, S, C, M, N, K);
+  if (rc) return rc;
+  if (a_row_stride < K || c_row_stride < N)
+    return fail(WQD_EINVAL, "%s: row pitches must cover the rows (a_row_stride=%u < K=%u or c_row_stride=%u < N=%u)",
+                fn, a_row_stride, K, c_row_stride, N);
+  if (a_row_stride % 8 != 0)
+    return fail(WQD_EINVAL, "%s: a_row_stride=%u is not a multiple of 8 (16-byte activation rows)", fn, a_row_stride);
+  if (static_cast<uint64_t>(M - 1) * a_row_stride + K > 0xFFFFFFFFull ||
+      static_cast<uint64_t>(M - 1) * c_row_stride + N > 0xFFFFFFFFull)
+    return fail(WQD_EINVAL, "%s: row pitches too large (the strided span exceeds 2^32 elements)", fn);
+  if ((rc = check_device(fn))) return rc;
+  (void)hipGetLastError();
+  return check_launch(fn, wqd::launch_w8a16_m16(A, W, S, C, M, N, K, a_row_stride, c_row_stride, 1, stream));
 }
 
 }  // extern "C"

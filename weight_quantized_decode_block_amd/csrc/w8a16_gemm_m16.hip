@@ -83,7 +83,7 @@ __device__ __forceinline__ bf16x8_t weights8(uint32_t lo4, uint32_t hi4) {
 struct ChunkMap {
   const uint8_t *W;
   const uint8_t *A;  // activations as bytes
-  uint32_t N, K, M, n0;
+  uint32_t N, K, M, n0, lda;  // lda: A row pitch in elements
 };
 
 __device__ __forceinline__ bool chunk_at(const ChunkMap &cm, uint32_t tid, int s, uint32_t p, uint32_t pbn,
@@ -100,7 +100,7 @@ __device__ __forceinline__ bool chunk_at(const ChunkMap &cm, uint32_t tid, int s
     const uint32_t c = (uint32_t)(s - 2) * kThreads + tid;
     const uint32_t m = c >> 7, col = c & 127u;
     ok = (m < cm.M) && (col < pbn * 16u);
-    a = cm.A + (size_t)m * cm.K * 2u + (size_t)p * (kPhaseBlocks * 256) + 16u * col;
+    a = cm.A + (size_t)m * cm.lda * 2u + (size_t)p * (kPhaseBlocks * 256) + 16u * col;
     off = kWBytes + m * kAPitch + 16u * col;
   }
   src = ok ? a : cm.W + (size_t)cm.n0 * cm.K;
@@ -160,7 +160,8 @@ __global__ __launch_bounds__(kThreads) void w8a16_gemm_m16_kernel(const uint16_t
                                                                   const uint8_t *__restrict__ W,
                                                                   const float *__restrict__ S,
                                                                   uint16_t *__restrict__ C, uint32_t M,
-                                                                  uint32_t N, uint32_t K) {
+                                                                  uint32_t N, uint32_t K, uint32_t lda,
+                                                                  uint32_t ldc, uint32_t band) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63u;
@@ -169,59 +170,65 @@ __global__ __launch_bounds__(kThreads) void w8a16_gemm_m16_kernel(const uint16_t
   const uint32_t nb = K >> 7;
   const uint32_t nphase = (nb + kPhaseBlocks - 1) / kPhaseBlocks;
   const uint32_t buf_bytes = (uint32_t)buffer_bytes(M);  // two buffers, then a 16-byte dummy slot
-  const ChunkMap cm{W, reinterpret_cast<const uint8_t *>(A), N, K, M, blockIdx.x * 16u};
-  const float *srow = S + (size_t)(cm.n0 >> 7) * nb;
-  const bool a_ok = i < M;
+  // tiles of this workgroup: `band` consecutive 16-row tiles from blockIdx.x * band
+  const uint32_t ntiles = (N + 15u) >> 4;
+  const uint32_t t_end = min(blockIdx.x * band + band, ntiles);
+  for (uint32_t t = blockIdx.x * band; t < t_end; ++t) {
+    const ChunkMap cm{W, reinterpret_cast<const uint8_t *>(A), N, K, M, 16u * t, lda};
+    const float *srow = S + (size_t)(cm.n0 >> 7) * nb;
+    const bool a_ok = i < M;
 
-  f32x4_t outer = {0.0f, 0.0f, 0.0f, 0.0f};
-  uint8_t *dummy = lds + 2u * buf_bytes;
-  // Blocks in phase q; 0 past the end, which turns every slot into a safe
-  // load that is written to the dummy slot.
-  auto blocks_in = [&](uint32_t q) { return q < nphase ? min((uint32_t)kPhaseBlocks, nb - q * kPhaseBlocks) : 0u; };
-  // One phase: store its chunks, request the phase kDepth ahead into the same
-  // registers, then compute on it.  Loads are issued in a fixed order with no
-  // branches around them, so each store waits only for its own phase's loads.
-  auto step = [&](uint32_t p, u32x4_t(&r)[SLOTS]) {
-    uint8_t *buf = lds + (p & 1u) * buf_bytes;
-    const uint32_t pbn = blocks_in(p);
-    write_phase<SLOTS>(cm, tid, p, pbn, r, buf, dummy);
-    issue_phase<SLOTS>(cm, tid, p + kDepth, blocks_in(p + kDepth), r);
-    __syncthreads();
-    if (wave < pbn) mac_block(buf, wave, i, g, a_ok, srow[p * kPhaseBlocks + wave], outer);
-  };
+    f32x4_t outer = {0.0f, 0.0f, 0.0f, 0.0f};
+    uint8_t *dummy = lds + 2u * buf_bytes;
+    // Blocks in phase q; 0 past the end, which turns every slot into a safe
+    // load that is written to the dummy slot.
+    auto blocks_in = [&](uint32_t q) { return q < nphase ? min((uint32_t)kPhaseBlocks, nb - q * kPhaseBlocks) : 0u; };
+    // One phase: store its chunks, request the phase kDepth ahead into the same
+    // registers, then compute on it.  Loads are issued in a fixed order with no
+    // branches around them, so each store waits only for its own phase's loads.
+    auto step = [&](uint32_t p, u32x4_t(&r)[SLOTS]) {
+      uint8_t *buf = lds + (p & 1u) * buf_bytes;
+      const uint32_t pbn = blocks_in(p);
+      write_phase<SLOTS>(cm, tid, p, pbn, r, buf, dummy);
+      issue_phase<SLOTS>(cm, tid, p + kDepth, blocks_in(p + kDepth), r);
+      __syncthreads();
+      if (wave < pbn) mac_block(buf, wave, i, g, a_ok, srow[p * kPhaseBlocks + wave], outer);
+    };
 
-  u32x4_t ring[kDepth][SLOTS];
+    u32x4_t ring[kDepth][SLOTS];
 #pragma unroll
-  for (int d = 0; d < kDepth; ++d) issue_phase<SLOTS>(cm, tid, d, blocks_in(d), ring[d]);
-  uint32_t p0 = 0;
-  for (; p0 + kDepth <= nphase; p0 += kDepth) {
+    for (int d = 0; d < kDepth; ++d) issue_phase<SLOTS>(cm, tid, d, blocks_in(d), ring[d]);
+    uint32_t p0 = 0;
+    for (; p0 + kDepth <= nphase; p0 += kDepth) {
 #pragma unroll
-    for (int d = 0; d < kDepth; ++d) step(p0 + d, ring[d]);
-  }
-#pragma unroll
-  for (int d = 0; d < kDepth; ++d)
-    if (p0 + d < nphase) step(p0 + d, ring[d]);
-
-  // Accumulator layout: this lane holds rows m = 4g + r of weight row n0 + i.
-  __syncthreads();
-  float *part = reinterpret_cast<float *>(lds);  // [wave][m][n]
-#pragma unroll
-  for (int r = 0; r < 4; ++r) part[(wave * 16u + 4u * g + r) * 16u + i] = outer[r];
-  __syncthreads();
-  if (tid < 256u) {
-    const uint32_t m = tid >> 4, col = tid & 15u;
-    const uint32_t n = cm.n0 + col;
-    if (m < M && n < N) {
-      float v = part[m * 16u + col];
-      for (uint32_t w = 1; w < kWaves; ++w) v = v + part[(w * 16u + m) * 16u + col];
-      C[(size_t)m * N + n] = f32_to_bf16_rne(v);
+      for (int d = 0; d < kDepth; ++d) step(p0 + d, ring[d]);
     }
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d)
+      if (p0 + d < nphase) step(p0 + d, ring[d]);
+
+    // Accumulator layout: this lane holds rows m = 4g + r of weight row n0 + i.
+    __syncthreads();
+    float *part = reinterpret_cast<float *>(lds);  // [wave][m][n]
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part[(wave * 16u + 4u * g + r) * 16u + i] = outer[r];
+    __syncthreads();
+    if (tid < 256u) {
+      const uint32_t m = tid >> 4, col = tid & 15u;
+      const uint32_t n = cm.n0 + col;
+      if (m < M && n < N) {
+        float v = part[m * 16u + col];
+        for (uint32_t w = 1; w < kWaves; ++w) v = v + part[(w * 16u + m) * 16u + col];
+        C[(size_t)m * ldc + n] = f32_to_bf16_rne(v);
+      }
+    }
+    __syncthreads();  // the partials sit in buffer 0, which the next tile's first phase overwrites
   }
 }
 
 template <int SLOTS>
 hipError_t launch_slots(const void *A, const void *W, const float *S, void *C, uint32_t M, uint32_t N,
-                        uint32_t K, hipStream_t stream) {
+                        uint32_t K, uint32_t lda, uint32_t ldc, uint32_t band, hipStream_t stream) {
   const size_t lds = 2 * (size_t)buffer_bytes((int)M) + 16;  // two buffers and the dummy slot
   static bool attr_set = false;  // one-time opt-in above the default LDS limit
   if (!attr_set) {
@@ -230,9 +237,10 @@ hipError_t launch_slots(const void *A, const void *W, const float *S, void *C, u
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(w8a16_gemm_m16_kernel<SLOTS>, dim3((N + 15) / 16), dim3(kThreads), lds, stream,
+  const uint32_t ntiles = (N + 15u) / 16u;
+  hipLaunchKernelGGL(w8a16_gemm_m16_kernel<SLOTS>, dim3((ntiles + band - 1u) / band), dim3(kThreads), lds, stream,
                      static_cast<const uint16_t *>(A), static_cast<const uint8_t *>(W), S,
-                     static_cast<uint16_t *>(C), M, N, K);
+                     static_cast<uint16_t *>(C), M, N, K, lda, ldc, band);
   return hipGetLastError();
 }
 
@@ -276,7 +284,8 @@ __global__ __launch_bounds__(kThreads) void w8a16_units_kernel(const uint16_t *_
                                                                const uint8_t *__restrict__ W,
                                                                const float *__restrict__ S,
                                                                uint16_t *__restrict__ C, uint32_t M, uint32_t N,
-                                                               uint32_t K) {
+                                                               uint32_t K, uint32_t lda, uint32_t ldc,
+                                                               uint32_t band) {
   using L = UnitLayout<MMAX>;
   constexpr int NF = MMAX < 4 ? MMAX : 4;  // accumulator rows that can hold outputs
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -286,7 +295,11 @@ __global__ __launch_bounds__(kThreads) void w8a16_units_kernel(const uint16_t *_
   const uint32_t i = lane & 15u, g = lane >> 4;
   const uint32_t nb = K >> 7;
   const uint32_t ntiles = (N + 15u) >> 4;
-  const uint32_t my_tiles = (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x;
+  // tiles of this workgroup: blockIdx.x, + gridDim.x, ... (band = 1), or the
+  // band of `band` consecutive tiles starting at blockIdx.x * band
+  const uint32_t t_first = band > 1u ? blockIdx.x * band : blockIdx.x;
+  const uint32_t t_step = band > 1u ? 1u : gridDim.x;
+  const uint32_t my_tiles = band > 1u ? min(band, ntiles - t_first) : (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x;
   // blocks of a tile owned by this wave: wave, wave + 8, ...; a wave that
   // owns none (K < 1024) runs one empty unit per tile to meet the barrier
   const uint32_t upw = nb > wave ? (nb - wave + kWaves - 1) / kWaves : 1u;
@@ -301,7 +314,7 @@ __global__ __launch_bounds__(kThreads) void w8a16_units_kernel(const uint16_t *_
   struct Cursor {
     uint32_t q, u, j, n0;  // unit, block index within the tile's share, tile index, tile's first row
   };
-  const uint32_t n0_step = 16u * gridDim.x;
+  const uint32_t n0_step = 16u * t_step;
   auto advance = [&](Cursor &c) {
     ++c.q;
     if (++c.u == upw) {
@@ -310,12 +323,12 @@ __global__ __launch_bounds__(kThreads) void w8a16_units_kernel(const uint16_t *_
       c.n0 += n0_step;
     }
   };
-  Cursor ld = {0u, 0u, 0u, 16u * blockIdx.x};
+  Cursor ld = {0u, 0u, 0u, 16u * t_first};
   const uint32_t w_lane = 32u * g;
   auto issue_next = [&]() {
     const bool live = ld.q < nq;
     const uint32_t b = min(wave + kWaves * ld.u, nb - 1u);
-    const uint32_t n0 = live ? ld.n0 : 16u * blockIdx.x;
+    const uint32_t n0 = live ? ld.n0 : 16u * t_first;
     const uint32_t row = min(n0 + i, N - 1u);
     const uint32_t voff = row * K + w_lane;
     const uint32_t soff = 128u * b;
@@ -344,7 +357,8 @@ __global__ __launch_bounds__(kThreads) void w8a16_units_kernel(const uint16_t *_
         const bool in = c < total;
         const uint32_t cc = in ? c : spare;
         const uint32_t m = cc / cpr, col = cc - m * cpr;
-        av[u] = *reinterpret_cast<const u32x4_t *>(reinterpret_cast<const uint8_t *>(A) + (size_t)cc * 16u);
+        av[u] = *reinterpret_cast<const u32x4_t *>(reinterpret_cast<const uint8_t *>(A) + (size_t)m * lda * 2u +
+                                                   16u * col);
         adst[u] = in ? L::kA + m * a_pitch + 16u * col : (uint32_t)L::kPart;  // idle: into the partials
       }
     };
@@ -378,7 +392,7 @@ __global__ __launch_bounds__(kThreads) void w8a16_units_kernel(const uint16_t *_
     for (int rr = 0; rr < NF; ++rr) outer[rr] = __fadd_rn(outer[rr], __fmul_rn(r.s, x[rr]));
   };
 
-  Cursor cc = {0u, 0u, 0u, 16u * blockIdx.x};
+  Cursor cc = {0u, 0u, 0u, 16u * t_first};
   auto step = [&](UnitRegs &r) {
     const uint32_t j = cc.j, u = cc.u, n0 = cc.n0;
     const uint32_t b = wave + kWaves * u;
@@ -401,7 +415,7 @@ __global__ __launch_bounds__(kThreads) void w8a16_units_kernel(const uint16_t *_
           const float *pp = part + (par * kWaves * MMAX + m) * 16u + col;
           float v = pp[0];
           for (uint32_t w = 1; w < kWaves; ++w) v = v + pp[w * MMAX * 16u];
-          C[(size_t)m * N + n] = f32_to_bf16_rne(v);
+          C[(size_t)m * ldc + n] = f32_to_bf16_rne(v);
         }
       }
       // this parity's partials are next written after the following tile's barrier
@@ -421,8 +435,9 @@ __global__ __launch_bounds__(kThreads) void w8a16_units_kernel(const uint16_t *_
 // at once, by registers (resolved once per kernel and process) and by LDS
 // (per call), each walking every gridDim.x-th tile.
 template <auto KERN>
-hipError_t launch_units(size_t lds, uint32_t ntiles, hipStream_t stream, const uint16_t *a, const uint8_t *w,
-                        const float *s, uint16_t *c, uint32_t M, uint32_t N, uint32_t K) {
+hipError_t launch_units(size_t lds, uint32_t ntiles, uint32_t band, hipStream_t stream, const uint16_t *a,
+                        const uint8_t *w, const float *s, uint16_t *c, uint32_t M, uint32_t N, uint32_t K,
+                        uint32_t lda, uint32_t ldc) {
   struct Res {
     hipError_t err = hipSuccess;
     int wg_per_cu = 1, cus = 1;
@@ -444,41 +459,41 @@ hipError_t launch_units(size_t lds, uint32_t ntiles, hipStream_t stream, const u
   const int by_lds = (int)((160u * 1024u) / lds);
   const int per_cu = by_lds < res.wg_per_cu ? (by_lds > 0 ? by_lds : 1) : res.wg_per_cu;
   const uint32_t resident = (uint32_t)(per_cu * res.cus);
-  const uint32_t grid = ntiles < resident ? ntiles : resident;
-  hipLaunchKernelGGL(KERN, dim3(grid), dim3(kThreads), lds, stream, a, w, s, c, M, N, K);
+  const uint32_t grid = band > 1u ? (ntiles + band - 1u) / band : (ntiles < resident ? ntiles : resident);
+  hipLaunchKernelGGL(KERN, dim3(grid), dim3(kThreads), lds, stream, a, w, s, c, M, N, K, lda, ldc, band);
   return hipGetLastError();
 }
 
 template <int MMAX>
 hipError_t launch_units_mmax(const void *A, const void *W, const float *S, void *C, uint32_t M, uint32_t N,
-                             uint32_t K, hipStream_t stream) {
+                             uint32_t K, uint32_t lda, uint32_t ldc, uint32_t band, hipStream_t stream) {
   const size_t lds = unit_lds_bytes<MMAX>(M, K);
   const uint32_t ntiles = (N + 15u) / 16u;
   const auto *a = static_cast<const uint16_t *>(A);
   const auto *w = static_cast<const uint8_t *>(W);
   auto *c = static_cast<uint16_t *>(C);
   const uint32_t per_thread = (M * (K >> 3) + kThreads - 1) / kThreads;
-  if (per_thread <= 2) return launch_units<w8a16_units_kernel<MMAX, 2, 2>>(lds, ntiles, stream, a, w, S, c, M, N, K);
-  if (per_thread <= 4) return launch_units<w8a16_units_kernel<MMAX, 2, 4>>(lds, ntiles, stream, a, w, S, c, M, N, K);
-  return launch_units<w8a16_units_kernel<MMAX, 2, 10>>(lds, ntiles, stream, a, w, S, c, M, N, K);
+  if (per_thread <= 2) return launch_units<w8a16_units_kernel<MMAX, 2, 2>>(lds, ntiles, band, stream, a, w, S, c, M, N, K, lda, ldc);
+  if (per_thread <= 4) return launch_units<w8a16_units_kernel<MMAX, 2, 4>>(lds, ntiles, band, stream, a, w, S, c, M, N, K, lda, ldc);
+  return launch_units<w8a16_units_kernel<MMAX, 2, 10>>(lds, ntiles, band, stream, a, w, S, c, M, N, K, lda, ldc);
 }
 
 }  // namespace
 
 hipError_t launch_w8a16_m16(const void *A, const void *W, const float *S, void *C, uint32_t M, uint32_t N,
-                            uint32_t K, hipStream_t stream) {
+                            uint32_t K, uint32_t lda, uint32_t ldc, uint32_t band, hipStream_t stream) {
   // the resident-activation kernel when A fits in LDS and the weights in one
   // buffer range; the per-phase kernel otherwise (same bits either way)
   const bool bounded = (uint64_t)N * K < (1ull << 31);
   if (bounded && M <= 8 && unit_lds_bytes<8>(M, K) <= 160u * 1024u) {
-    if (M <= 1) return launch_units_mmax<1>(A, W, S, C, M, N, K, stream);
-    if (M <= 2) return launch_units_mmax<2>(A, W, S, C, M, N, K, stream);
-    if (M <= 4) return launch_units_mmax<4>(A, W, S, C, M, N, K, stream);
-    return launch_units_mmax<8>(A, W, S, C, M, N, K, stream);
+    if (M <= 1) return launch_units_mmax<1>(A, W, S, C, M, N, K, lda, ldc, band, stream);
+    if (M <= 2) return launch_units_mmax<2>(A, W, S, C, M, N, K, lda, ldc, band, stream);
+    if (M <= 4) return launch_units_mmax<4>(A, W, S, C, M, N, K, lda, ldc, band, stream);
+    return launch_units_mmax<8>(A, W, S, C, M, N, K, lda, ldc, band, stream);
   }
-  if (M <= 4) return launch_slots<slots_for(4)>(A, W, S, C, M, N, K, stream);
-  if (M <= 8) return launch_slots<slots_for(8)>(A, W, S, C, M, N, K, stream);
-  return launch_slots<slots_for(16)>(A, W, S, C, M, N, K, stream);
+  if (M <= 4) return launch_slots<slots_for(4)>(A, W, S, C, M, N, K, lda, ldc, band, stream);
+  if (M <= 8) return launch_slots<slots_for(8)>(A, W, S, C, M, N, K, lda, ldc, band, stream);
+  return launch_slots<slots_for(16)>(A, W, S, C, M, N, K, lda, ldc, band, stream);
 }
 
 }  // namespace wqd
