@@ -174,7 +174,7 @@ int w8a16_gemm_m16(const void *A, const void *W, const float *S, void *C, uint32
   if (rc) return rc;
   if ((rc = check_device(fn))) return rc;
   (void)hipGetLastError();
-  return check_launch(fn, wqd::launch_w8a16_m16(A, W, S, C, M, N, K, K, N, 1, stream));
+  return check_launch(fn, wqd::launch_w8a16_m16(A, W, S, C, M, N, K, K, N, 0, stream));
 }
 
 int w8a16_gemm_m16_n64(const void *A, const void *W, const float *S, void *C, uint32_t M, uint32_t N,
@@ -202,7 +202,7 @@ int w8a16_gemm_m16_strided(const void *A, const void *W, const float *S, void *C
     return fail(WQD_EINVAL, "%s: row pitches too large (the strided span exceeds 2^32 elements)", fn);
   if ((rc = check_device(fn))) return rc;
   (void)hipGetLastError();
-  return check_launch(fn, wqd::launch_w8a16_m16(A, W, S, C, M, N, K, a_row_stride, c_row_stride, 1, stream));
+  return check_launch(fn, wqd::launch_w8a16_m16(A, W, S, C, M, N, K, a_row_stride, c_row_stride, 0, stream));
 }
 
 }  // extern "C"

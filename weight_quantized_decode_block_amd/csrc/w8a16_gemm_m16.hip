@@ -238,6 +238,7 @@ hipError_t launch_slots(const void *A, const void *W, const float *S, void *C, u
     attr_set = true;
   }
   const uint32_t ntiles = (N + 15u) / 16u;
+  if (band == 0u) band = 1u;  // one tile per workgroup
   hipLaunchKernelGGL(w8a16_gemm_m16_kernel<SLOTS>, dim3((ntiles + band - 1u) / band), dim3(kThreads), lds, stream,
                      static_cast<const uint16_t *>(A), static_cast<const uint8_t *>(W), S,
                      static_cast<uint16_t *>(C), M, N, K, lda, ldc, band);
@@ -251,18 +252,28 @@ hipError_t launch_slots(const void *A, const void *W, const float *S, void *C, u
 // above, so both give the same bits.  Weight bytes go straight from memory to
 // the lanes that use them, and each wave works on its own blocks without
 // waiting for the others until the end of a tile.
-//   * A workgroup of 8 waves walks its tiles of 16 weight rows (blockIdx.x,
-//     + gridDim.x, ...); wave w owns blocks w, w + 8, ... of every tile.
+//   * A workgroup of 8 waves owns a contiguous range of weight rows and walks
+//     it in tiles of 16 rows (the last one may be partial); wave w owns
+//     blocks w, w + 8, ... of every tile.  The ranges are either an even
+//     split of the N rows over the grid (one workgroup per CU, so every CU
+//     streams the same number of bytes: with 16-row tiles dealt out whole,
+//     5120 rows are 320 tiles and a quarter of the CUs would stream twice as
+//     much as the rest), or bands of 16 * band rows.
 //   * Per block, lane (i, g) loads the 32 weights k = 32g..32g+31 of row
-//     n0 + i (two 16-byte buffer loads, bounded by the matrix size; rows past
-//     N re-read row N - 1) and the block's scale (a uniform 4-byte load),
-//     DEPTH blocks ahead of the compute.
+//     n0 + i (two 16-byte buffer loads; a lane whose row lies outside the
+//     range gives an offset past the end of the buffer, which the hardware
+//     range check turns into zeros without a memory access) and the block's
+//     scale for that row (4 bytes), DEPTH blocks ahead of the compute.
 //   * Activations are copied into LDS once per workgroup; lane (i, g) reads
 //     its 64 bytes of row i (rows i >= M read row 0 and feed outputs that are
 //     never stored).
 //   * At the end of a tile the 8 waves' accumulators are added in LDS in wave
 //     order and rows m < M are stored.
 // ---------------------------------------------------------------------------
+// Buffer offset of a lane with no row: beyond every weight buffer the kernel
+// accepts (N * K < 2^31), and still below 2^32 after adding a block offset.
+constexpr uint32_t kPastEnd = 0x80000000u;
+
 struct UnitRegs {
   u32x4_t w0, w1;  // this lane's 32 FP8 weights of the block
   float s;         // the block's scale
@@ -294,12 +305,17 @@ __global__ __launch_bounds__(kThreads) void w8a16_units_kernel(const uint16_t *_
   const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t i = lane & 15u, g = lane >> 4;
   const uint32_t nb = K >> 7;
-  const uint32_t ntiles = (N + 15u) >> 4;
-  // tiles of this workgroup: blockIdx.x, + gridDim.x, ... (band = 1), or the
-  // band of `band` consecutive tiles starting at blockIdx.x * band
-  const uint32_t t_first = band > 1u ? blockIdx.x * band : blockIdx.x;
-  const uint32_t t_step = band > 1u ? 1u : gridDim.x;
-  const uint32_t my_tiles = band > 1u ? min(band, ntiles - t_first) : (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x;
+  // rows [r0, r1) of this workgroup: an even split over the grid (band = 0) or
+  // 16 * band rows from blockIdx.x * 16 * band
+  uint32_t r0, r1;
+  if (band == 0u) {
+    r0 = (uint32_t)(((uint64_t)N * blockIdx.x) / gridDim.x);
+    r1 = (uint32_t)(((uint64_t)N * (blockIdx.x + 1u)) / gridDim.x);
+  } else {
+    r0 = blockIdx.x * 16u * band;
+    r1 = min(r0 + 16u * band, N);
+  }
+  const uint32_t my_tiles = (r1 - r0 + 15u) >> 4;
   // blocks of a tile owned by this wave: wave, wave + 8, ...; a wave that
   // owns none (K < 1024) runs one empty unit per tile to meet the barrier
   const uint32_t upw = nb > wave ? (nb - wave + kWaves - 1) / kWaves : 1u;
@@ -314,28 +330,29 @@ __global__ __launch_bounds__(kThreads) void w8a16_units_kernel(const uint16_t *_
   struct Cursor {
     uint32_t q, u, j, n0;  // unit, block index within the tile's share, tile index, tile's first row
   };
-  const uint32_t n0_step = 16u * t_step;
   auto advance = [&](Cursor &c) {
     ++c.q;
     if (++c.u == upw) {
       c.u = 0;
       ++c.j;
-      c.n0 += n0_step;
+      c.n0 += 16u;
     }
   };
-  Cursor ld = {0u, 0u, 0u, 16u * t_first};
+  Cursor ld = {0u, 0u, 0u, r0};
   const uint32_t w_lane = 32u * g;
   auto issue_next = [&]() {
     const bool live = ld.q < nq;
     const uint32_t b = min(wave + kWaves * ld.u, nb - 1u);
-    const uint32_t n0 = live ? ld.n0 : 16u * t_first;
-    const uint32_t row = min(n0 + i, N - 1u);
-    const uint32_t voff = row * K + w_lane;
+    const uint32_t n0 = live ? ld.n0 : r0;
+    const uint32_t row = n0 + i;
+    const uint32_t voff = row < r1 ? row * K + w_lane : kPastEnd;
     const uint32_t soff = 128u * b;
     UnitRegs r;
     r.w0 = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, voff, soff, 0);
     r.w1 = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, voff + 16u, soff, 0);
-    r.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srsrc, 0u, ((n0 >> 7) * nb + b) * 4u, 0));
+    // the scale of this lane's own row: a tile need not sit inside one 128-row scale group
+    const uint32_t srow = (row < r1 ? row : r1 - 1u) >> 7;
+    r.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srsrc, srow * nb * 4u, 4u * b, 0));
     advance(ld);
     return r;
   };
@@ -392,7 +409,7 @@ __global__ __launch_bounds__(kThreads) void w8a16_units_kernel(const uint16_t *_
     for (int rr = 0; rr < NF; ++rr) outer[rr] = __fadd_rn(outer[rr], __fmul_rn(r.s, x[rr]));
   };
 
-  Cursor cc = {0u, 0u, 0u, 16u * t_first};
+  Cursor cc = {0u, 0u, 0u, r0};
   auto step = [&](UnitRegs &r) {
     const uint32_t j = cc.j, u = cc.u, n0 = cc.n0;
     const uint32_t b = wave + kWaves * u;
@@ -411,7 +428,7 @@ __global__ __launch_bounds__(kThreads) void w8a16_units_kernel(const uint16_t *_
       if (tid < M * 16u) {
         const uint32_t m = tid >> 4, col = tid & 15u;
         const uint32_t n = n0 + col;
-        if (n < N) {
+        if (n < r1) {
           const float *pp = part + (par * kWaves * MMAX + m) * 16u + col;
           float v = pp[0];
           for (uint32_t w = 1; w < kWaves; ++w) v = v + pp[w * MMAX * 16u];
@@ -431,9 +448,11 @@ __global__ __launch_bounds__(kThreads) void w8a16_units_kernel(const uint16_t *_
     if (cc.q < nq) step(ring[d]);
 }
 
-// Launches KERN as a persistent grid: as many workgroups as fit on the device
-// at once, by registers (resolved once per kernel and process) and by LDS
-// (per call), each walking every gridDim.x-th tile.
+// Launches KERN with one workgroup per 64-row band (band > 0), or with
+// kUnitWgsPerCu workgroups per CU (fewer if registers or LDS do not allow it,
+// and never fewer than 16 rows per workgroup) splitting the rows evenly.
+constexpr int kUnitWgsPerCu = 1;
+
 template <auto KERN>
 hipError_t launch_units(size_t lds, uint32_t ntiles, uint32_t band, hipStream_t stream, const uint16_t *a,
                         const uint8_t *w, const float *s, uint16_t *c, uint32_t M, uint32_t N, uint32_t K,
@@ -457,9 +476,10 @@ hipError_t launch_units(size_t lds, uint32_t ntiles, uint32_t band, hipStream_t 
   }();
   if (res.err != hipSuccess) return res.err;
   const int by_lds = (int)((160u * 1024u) / lds);
-  const int per_cu = by_lds < res.wg_per_cu ? (by_lds > 0 ? by_lds : 1) : res.wg_per_cu;
+  int per_cu = by_lds < res.wg_per_cu ? (by_lds > 0 ? by_lds : 1) : res.wg_per_cu;
+  if (per_cu > kUnitWgsPerCu) per_cu = kUnitWgsPerCu;
   const uint32_t resident = (uint32_t)(per_cu * res.cus);
-  const uint32_t grid = band > 1u ? (ntiles + band - 1u) / band : (ntiles < resident ? ntiles : resident);
+  const uint32_t grid = band > 0u ? (ntiles + band - 1u) / band : (ntiles < resident ? ntiles : resident);
   hipLaunchKernelGGL(KERN, dim3(grid), dim3(kThreads), lds, stream, a, w, s, c, M, N, K, lda, ldc, band);
   return hipGetLastError();
 }
@@ -473,9 +493,9 @@ hipError_t launch_units_mmax(const void *A, const void *W, const float *S, void 
   const auto *w = static_cast<const uint8_t *>(W);
   auto *c = static_cast<uint16_t *>(C);
   const uint32_t per_thread = (M * (K >> 3) + kThreads - 1) / kThreads;
-  if (per_thread <= 2) return launch_units<w8a16_units_kernel<MMAX, 2, 2>>(lds, ntiles, band, stream, a, w, S, c, M, N, K, lda, ldc);
-  if (per_thread <= 4) return launch_units<w8a16_units_kernel<MMAX, 2, 4>>(lds, ntiles, band, stream, a, w, S, c, M, N, K, lda, ldc);
-  return launch_units<w8a16_units_kernel<MMAX, 2, 10>>(lds, ntiles, band, stream, a, w, S, c, M, N, K, lda, ldc);
+  if (per_thread <= 2) return launch_units<w8a16_units_kernel<MMAX, 4, 2>>(lds, ntiles, band, stream, a, w, S, c, M, N, K, lda, ldc);
+  if (per_thread <= 4) return launch_units<w8a16_units_kernel<MMAX, 4, 4>>(lds, ntiles, band, stream, a, w, S, c, M, N, K, lda, ldc);
+  return launch_units<w8a16_units_kernel<MMAX, 4, 10>>(lds, ntiles, band, stream, a, w, S, c, M, N, K, lda, ldc);
 }
 
 }  // namespace

@@ -18,9 +18,9 @@ hipError_t launch_q2_0_mfma(const void *A, const void *B, void *C, uint32_t N,
                             uint32_t K, uint32_t m, hipStream_t stream);
 
 // Enqueue the W8A16 M16 GEMM for 1..16 rows; A and C row pitches lda / ldc
-// in elements; band = 1 (workgroups walk tiles spread over the matrix) or 4
-// (each workgroup owns 64 consecutive weight rows).  Shapes validated by the
-// caller.
+// in elements; band = 0 (the weight rows split evenly over the workgroups) or
+// b > 0 (each workgroup owns 16 * b consecutive weight rows).  Every choice
+// gives the same bits.  Shapes validated by the caller.
 hipError_t launch_w8a16_m16(const void *A, const void *W, const float *S,
                             void *C, uint32_t M, uint32_t N, uint32_t K,
                             uint32_t lda, uint32_t ldc, uint32_t band,
