@@ -160,6 +160,41 @@ int w8a16_gemm_m16_strided(const void *A, const void *W, const float *S, void *C
                            uint32_t a_row_stride, uint32_t c_row_stride,
                            hipStream_t stream);
 
+/*
+ * w8a16_gemv_batch16 - W8A16 decode GEMV on the vector ALUs for 1..16 rows:
+ * the same operation as w8a16_gemm_m16 (FP8 E4M3FN weights, 128x128 fp32
+ * block scales folded once per 128-K block onto an fp32 outer accumulator),
+ * computed without matrix instructions.
+ * Defined by page "w8a16_gemm_m16.rs", module doc (the scalar GEMV
+ * w8a16_gemv_batch16 beside the matrix-core kernel, one multiply-add per
+ * weight byte and activation row, not bit-identical to the matrix-core
+ * kernel) and the scale-fold rule stated there.
+ *
+ *   A, W, S, C, M, N, K as for w8a16_gemm_m16 (M 1..16, K a multiple of 128)
+ *   K must also be at most 81920 (one activation row is staged on chip):
+ *     larger K gives WQD_EUNSUPPORTED
+ *
+ * Rows are served by launches of at most 8 rows (fewer when 8 rows of K do not
+ * fit on chip), A and C advanced by whole rows.  Matches the CPU reference
+ * within 2 BF16 ulp or 1e-2 of the row RMS; each output row is bit-identical
+ * for every M (its arithmetic does not depend on the other rows), but not to
+ * w8a16_gemm_m16, whose matrix instructions add in their own order.
+ */
+int w8a16_gemv_batch16(const void *A, const void *W, const float *S, void *C,
+                       uint32_t M, uint32_t N, uint32_t K, hipStream_t stream);
+
+/*
+ * w8a16_gemv_batch16_strided - w8a16_gemv_batch16 with A and C row pitches,
+ * with the argument order and pitch rules of w8a16_gemm_m16_strided (page
+ * "w8a16_gemm_m16.rs", doc of w8a16_gemm_m16_strided, which names the
+ * strided scalar GEMV as having the same argument order).  Each output row is
+ * bit-identical to w8a16_gemv_batch16 on the same row stored contiguously.
+ */
+int w8a16_gemv_batch16_strided(const void *A, const void *W, const float *S, void *C,
+                               uint32_t M, uint32_t N, uint32_t K,
+                               uint32_t a_row_stride, uint32_t c_row_stride,
+                               hipStream_t stream);
+
 /* ----------------------------------------------------------- host helpers */
 
 /* Bytes of a packed Q2_0 matrix: N * (K/128) * 34, or 0 if K % 128 != 0. */

@@ -29,7 +29,8 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = wqd.header_functions()
     assert set(names) >= {"q2_0_gemv", "q2_0_gemv_batchm", "w8a16_gemm_m16", "w8a16_gemm_m16_n64",
-                          "w8a16_gemm_m16_strided", "q2_0_packed_bytes", "q2_0_pack",
+                          "w8a16_gemm_m16_strided", "w8a16_gemv_batch16", "w8a16_gemv_batch16_strided",
+                          "q2_0_packed_bytes", "q2_0_pack",
                           "q2_0_batchm_chunks", "wqd_last_error"}
     for n in names:
         assert hasattr(L, n), n
@@ -75,7 +76,8 @@ def test_q2_0_batchm_validation(L):
     ((FAKE, FAKE + 4, FAKE, FAKE, 16, 64, 1024), wqd.WQD_EALIGN, "W must"),
     ((FAKE, FAKE, FAKE + 2, FAKE, 16, 64, 1024), wqd.WQD_EALIGN, "S must"),
 ])
-@pytest.mark.parametrize("fn", ["w8a16_gemm_m16", "w8a16_gemm_m16_n64", "w8a16_gemm_m16_strided"])
+@pytest.mark.parametrize("fn", ["w8a16_gemm_m16", "w8a16_gemm_m16_n64", "w8a16_gemm_m16_strided",
+                                "w8a16_gemv_batch16", "w8a16_gemv_batch16_strided"])
 def test_w8a16_validation(L, fn, args, code, frag):
     """The three W8A16 entry points share the guards of page "w8a16_gemm_m16.rs"."""
     extra = (args[6], args[5]) if fn.endswith("_strided") else ()  # pitches = K, N
@@ -93,11 +95,29 @@ def test_w8a16_validation(L, fn, args, code, frag):
     (16, 64, 1024, 0x12000000, 64, "too large"),   # 15 * pitch + K >= 2^32
     (16, 64, 1024, 1024, 0x12000000, "too large"),
 ])
-def test_w8a16_strided_validation(L, M, N, K, lda, ldc, frag):
+@pytest.mark.parametrize("fn", ["w8a16_gemm_m16_strided", "w8a16_gemv_batch16_strided"])
+def test_w8a16_strided_validation(L, fn, M, N, K, lda, ldc, frag):
     """Pitch rules of page "w8a16_gemm_m16.rs" (doc of w8a16_gemm_m16_strided)."""
-    rc = L.w8a16_gemm_m16_strided(FAKE, FAKE, FAKE, FAKE, M, N, K, lda, ldc, None)
+    rc = getattr(L, fn)(FAKE, FAKE, FAKE, FAKE, M, N, K, lda, ldc, None)
     assert rc == wqd.WQD_EINVAL
     assert frag in wqd.last_error()
+
+
+@pytest.mark.parametrize("K,code", [(81920, None), (82048, wqd.WQD_EUNSUPPORTED), (1 << 20, wqd.WQD_EUNSUPPORTED)])
+def test_w8a16_gemv_k_limit(L, K, code):
+    """The vector-ALU GEMV stages one activation row on chip: K <= 81920."""
+    if code is None:  # a valid call: only checked where no GPU could run it on the fake pointers
+        try:
+            import torch
+            if torch.cuda.is_available():
+                pytest.skip("a GPU is present")
+        except ImportError:
+            pass
+    rc = L.w8a16_gemv_batch16(FAKE, FAKE, FAKE, FAKE, 1, 64, K, None)
+    if code is None:
+        assert rc in (wqd.WQD_ENODEV, wqd.WQD_EHIP)
+    else:
+        assert rc == code and "81920" in wqd.last_error()
 
 
 @pytest.mark.parametrize("lda,ldc", [(1024, 64), (1032, 65), (4096, 1000)])

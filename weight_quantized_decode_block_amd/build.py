@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libwqd.so")
-SOURCES = ["api.cpp", "pack.cpp", "q2_0_mfma.hip", "q2_0_valu.hip", "w8a16_gemm_m16.hip"]
+SOURCES = ["api.cpp", "pack.cpp", "q2_0_mfma.hip", "q2_0_valu.hip", "w8a16_gemm_m16.hip", "w8a16_gemv.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -111,6 +111,22 @@ int validate_w8a16(const char *fn, const void *A, const void *W, const float *S,
   return WQD_OK;
 }
 
+// Row pitches of the strided entry points (page "w8a16_gemm_m16.rs", doc of
+// w8a16_gemm_m16_strided): each covers its row, the activation pitch keeps
+// rows 16-byte aligned, and the strided span fits 32-bit element offsets.
+int validate_pitches(const char *fn, uint32_t M, uint32_t N, uint32_t K, uint32_t a_row_stride,
+                     uint32_t c_row_stride) {
+  if (a_row_stride < K || c_row_stride < N)
+    return fail(WQD_EINVAL, "%s: row pitches must cover the rows (a_row_stride=%u < K=%u or c_row_stride=%u < N=%u)",
+                fn, a_row_stride, K, c_row_stride, N);
+  if (a_row_stride % 8 != 0)
+    return fail(WQD_EINVAL, "%s: a_row_stride=%u is not a multiple of 8 (16-byte activation rows)", fn, a_row_stride);
+  if (static_cast<uint64_t>(M - 1) * a_row_stride + K > 0xFFFFFFFFull ||
+      static_cast<uint64_t>(M - 1) * c_row_stride + N > 0xFFFFFFFFull)
+    return fail(WQD_EINVAL, "%s: row pitches too large (the strided span exceeds 2^32 elements)", fn);
+  return WQD_OK;
+}
+
 // 16-row tiles per workgroup in w8a16_gemm_m16_n64: 64 weight rows each.
 constexpr uint32_t kN64Band = 4;
 
@@ -192,17 +208,38 @@ int w8a16_gemm_m16_strided(const void *A, const void *W, const float *S, void *C
   static const char fn[] = "w8a16_gemm_m16_strided";
   int rc = validate_w8a16(fn, A, W, S, C, M, N, K);
   if (rc) return rc;
-  if (a_row_stride < K || c_row_stride < N)
-    return fail(WQD_EINVAL, "%s: row pitches must cover the rows (a_row_stride=%u < K=%u or c_row_stride=%u < N=%u)",
-                fn, a_row_stride, K, c_row_stride, N);
-  if (a_row_stride % 8 != 0)
-    return fail(WQD_EINVAL, "%s: a_row_stride=%u is not a multiple of 8 (16-byte activation rows)", fn, a_row_stride);
-  if (static_cast<uint64_t>(M - 1) * a_row_stride + K > 0xFFFFFFFFull ||
-      static_cast<uint64_t>(M - 1) * c_row_stride + N > 0xFFFFFFFFull)
-    return fail(WQD_EINVAL, "%s: row pitches too large (the strided span exceeds 2^32 elements)", fn);
+  if ((rc = validate_pitches(fn, M, N, K, a_row_stride, c_row_stride))) return rc;
   if ((rc = check_device(fn))) return rc;
   (void)hipGetLastError();
   return check_launch(fn, wqd::launch_w8a16_m16(A, W, S, C, M, N, K, a_row_stride, c_row_stride, 0, stream));
+}
+
+int w8a16_gemv_batch16_strided(const void *A, const void *W, const float *S, void *C, uint32_t M, uint32_t N,
+                               uint32_t K, uint32_t a_row_stride, uint32_t c_row_stride, hipStream_t stream) {
+  static const char fn[] = "w8a16_gemv_batch16_strided";
+  int rc = validate_w8a16(fn, A, W, S, C, M, N, K);
+  if (rc) return rc;
+  if ((rc = validate_pitches(fn, M, N, K, a_row_stride, c_row_stride))) return rc;
+  const uint32_t rows = wqd::w8a16_gemv_rows_per_launch(K);
+  if (rows == 0)
+    return fail(WQD_EUNSUPPORTED, "%s: K=%u above 81920 (one activation row must fit in LDS)", fn, K);
+  if ((rc = check_device(fn))) return rc;
+  (void)hipGetLastError();
+  const uint16_t *a = static_cast<const uint16_t *>(A);
+  uint16_t *c = static_cast<uint16_t *>(C);
+  for (uint32_t r0 = 0; r0 < M; r0 += rows) {
+    const uint32_t m = (M - r0) < rows ? (M - r0) : rows;
+    rc = check_launch(fn, wqd::launch_w8a16_gemv(a + static_cast<size_t>(r0) * a_row_stride, W, S,
+                                                 c + static_cast<size_t>(r0) * c_row_stride, m, N, K,
+                                                 a_row_stride, c_row_stride, stream));
+    if (rc) return rc;
+  }
+  return WQD_OK;
+}
+
+int w8a16_gemv_batch16(const void *A, const void *W, const float *S, void *C, uint32_t M, uint32_t N, uint32_t K,
+                       hipStream_t stream) {
+  return w8a16_gemv_batch16_strided(A, W, S, C, M, N, K, K, N, stream);
 }
 
 }  // extern "C"

@@ -26,4 +26,15 @@ hipError_t launch_w8a16_m16(const void *A, const void *W, const float *S,
                             uint32_t lda, uint32_t ldc, uint32_t band,
                             hipStream_t stream);
 
+// Enqueue the vector-ALU W8A16 GEMV for 1..w8a16_gemv_rows_per_launch(K)
+// rows (at most 8); A and C row pitches lda / ldc in elements.  Shapes
+// validated by the caller.
+hipError_t launch_w8a16_gemv(const void *A, const void *W, const float *S,
+                             void *C, uint32_t M, uint32_t N, uint32_t K,
+                             uint32_t lda, uint32_t ldc, hipStream_t stream);
+
+// Activation rows one vector-ALU GEMV launch can stage in LDS (0 when one
+// row of K does not fit).
+uint32_t w8a16_gemv_rows_per_launch(uint32_t K);
+
 }  // namespace wqd

@@ -49,8 +49,10 @@ def lib() -> ctypes.CDLL:
     L.w8a16_gemm_m16.argtypes = [vp, vp, vp, vp, u32, u32, u32, vp]
     L.w8a16_gemm_m16_n64.argtypes = [vp, vp, vp, vp, u32, u32, u32, vp]
     L.w8a16_gemm_m16_strided.argtypes = [vp, vp, vp, vp, u32, u32, u32, u32, u32, vp]
+    L.w8a16_gemv_batch16.argtypes = [vp, vp, vp, vp, u32, u32, u32, vp]
+    L.w8a16_gemv_batch16_strided.argtypes = [vp, vp, vp, vp, u32, u32, u32, u32, u32, vp]
     for f in (L.q2_0_gemv, L.q2_0_gemv_batchm, L.w8a16_gemm_m16, L.w8a16_gemm_m16_n64,
-              L.w8a16_gemm_m16_strided):
+              L.w8a16_gemm_m16_strided, L.w8a16_gemv_batch16, L.w8a16_gemv_batch16_strided):
         f.restype = ctypes.c_int
     L.q2_0_packed_bytes.argtypes = [u32, u32]
     L.q2_0_packed_bytes.restype = sz
@@ -132,6 +134,18 @@ def w8a16_gemm_m16_strided(A, W, S, C, M: int, N: int, K: int, a_row_stride: int
     _check("w8a16_gemm_m16_strided",
            lib().w8a16_gemm_m16_strided(_ptr(A), _ptr(W), _ptr(S), _ptr(C), M, N, K, a_row_stride,
                                         c_row_stride, _stream(stream)))
+
+
+def w8a16_gemv_batch16(A, W, S, C, M: int, N: int, K: int, stream=None) -> None:
+    _check("w8a16_gemv_batch16",
+           lib().w8a16_gemv_batch16(_ptr(A), _ptr(W), _ptr(S), _ptr(C), M, N, K, _stream(stream)))
+
+
+def w8a16_gemv_batch16_strided(A, W, S, C, M: int, N: int, K: int, a_row_stride: int, c_row_stride: int,
+                               stream=None) -> None:
+    _check("w8a16_gemv_batch16_strided",
+           lib().w8a16_gemv_batch16_strided(_ptr(A), _ptr(W), _ptr(S), _ptr(C), M, N, K, a_row_stride,
+                                            c_row_stride, _stream(stream)))
 
 
 # ------------------------------------------------------------ host helpers
