@@ -15,15 +15,16 @@
 // Work layout
 //   * One workgroup of 8 waves per CU owns an even share [r0, r1) of the N
 //     weight rows; wave w takes rows r0 + w, r0 + w + 8, ... in groups of
-//     kRpw rows.
+//     RPW rows (as many as the wave holds, up to 3).
 //   * A weight row is read in chunks of 1024 k: lane l loads the 16 FP8
 //     weights k0 = 1024c + 16l .. k0 + 15 with one 16-byte load, so every load
 //     instruction covers 1 KB of consecutive bytes; lanes 8j .. 8j + 7 hold
 //     block b = 8c + j.  Lanes past the end of the row load through an offset
 //     beyond the buffer, which the hardware range check turns into zeros.
 //   * Within a group the wave goes chunk-major (chunk c of each of the
-//     group's rows, then chunk c + 1), with kDepth row-chunks of loads in
-//     flight.  The activations are staged once per workgroup in LDS, laid out
+//     group's rows, then chunk c + 1), with two groups' row-chunks of loads
+//     in flight; they are issued once the activations are in LDS (issuing
+//     them earlier delays the activations behind them).  The activations are staged once per workgroup in LDS, laid out
 //     so that the two 16-byte reads of a lane's 16 activations are each
 //     contiguous across the wave, and read into registers at the first row of
 //     every chunk.
@@ -55,8 +56,6 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kWaves = 8;
 constexpr uint32_t kThreads = 64 * kWaves;
-constexpr int kRpw = 4;                 // rows per wave group
-constexpr int kDepth = 2 * kRpw;        // row-chunks of loads in flight per wave
 constexpr uint32_t kChunkBytes = 2048;  // LDS bytes of one activation row's 1024-k chunk
 constexpr uint32_t kPastEnd = 0x80000000u;
 constexpr uint32_t kMaxRowsPerLaunch = 8;
@@ -84,12 +83,23 @@ constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;  // lane i <- lane 7 - i within 8
 
+// f(integral_constant<D>) for D = B .. E-1, unrolled at compile time
+template <int B, int E, typename F>
+__device__ __forceinline__ void unroll(F &&f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    unroll<B + 1, E>(f);
+  }
+}
+
 struct ChunkRegs {
   u32x4_t w;  // 16 FP8 weights of one row-chunk
   float s;    // the scale of this lane's block
 };
 
-template <int MMAX>
+// RPW: rows per wave group; DEPTH: row-chunks of loads in flight per wave (a
+// multiple of RPW, so a ring position always serves the same row slot)
+template <int MMAX, int RPW, int DEPTH>
 __global__ __launch_bounds__(kThreads) void w8a16_gemv_kernel(const uint16_t *__restrict__ A,
                                                               const uint8_t *__restrict__ W,
                                                               const float *__restrict__ S,
@@ -104,19 +114,19 @@ __global__ __launch_bounds__(kThreads) void w8a16_gemv_kernel(const uint16_t *__
   const uint32_t a_pitch = nchunk * kChunkBytes;
   const uint32_t r0 = (uint32_t)(((uint64_t)N * blockIdx.x) / gridDim.x);
   const uint32_t r1 = (uint32_t)(((uint64_t)N * (blockIdx.x + 1u)) / gridDim.x);
-  // rows of this wave: r0 + wave + 8t for t < nrows, in groups of kRpw
+  // rows of this wave: r0 + wave + 8t for t < nrows, in groups of RPW
   const uint32_t nrows = r1 - r0 > wave ? (r1 - r0 - wave + kWaves - 1u) / kWaves : 0u;
-  const uint32_t ngroups = (nrows + kRpw - 1u) / kRpw;
-  const uint32_t nq = ngroups * nchunk * kRpw;  // row-chunks, padded to whole groups
+  const uint32_t ngroups = (nrows + RPW - 1u) / RPW;
+  const uint32_t nq = ngroups * nchunk * RPW;  // row-chunks, padded to whole groups
   const uint32_t k_lane = 16u * lane;           // + 1024c: this lane's first k of a chunk
 
   // Work cursor: row slot t of group grp, chunk c.
   struct Cursor {
     uint32_t q, t, c, grp;
   };
-  auto advance = [&](Cursor &cu) {
+  auto advance = [&](Cursor &cu) __attribute__((always_inline)) {
     ++cu.q;
-    if (++cu.t == (uint32_t)kRpw) {
+    if (++cu.t == (uint32_t)RPW) {
       cu.t = 0;
       if (++cu.c == nchunk) {
         cu.c = 0;
@@ -125,8 +135,8 @@ __global__ __launch_bounds__(kThreads) void w8a16_gemv_kernel(const uint16_t *__
     }
   };
   Cursor ld = {0u, 0u, 0u, 0u};
-  auto issue_next = [&]() {
-    const uint32_t ti = ld.grp * kRpw + ld.t;  // row index within the wave
+  auto issue_next = [&]() __attribute__((always_inline)) {
+    const uint32_t ti = ld.grp * RPW + ld.t;  // row index within the wave
     const bool live = ld.q < nq && ti < nrows;
     const uint32_t n = live ? r0 + wave + kWaves * ti : r0;
     const uint32_t k0 = 1024u * ld.c + k_lane;
@@ -142,12 +152,13 @@ __global__ __launch_bounds__(kThreads) void w8a16_gemv_kernel(const uint16_t *__
     return r;
   };
 
-  ChunkRegs ring[kDepth];
+  static_assert(DEPTH % RPW == 0, "a ring position must always serve the same row slot");
+  ChunkRegs ring[DEPTH];
   {  // activations into LDS: 16-byte piece p of chunk c of row m holds
      // A[m][1024c + 8p .. +7] at m * a_pitch + 2048c + 1024(p & 1) + 16(p >> 1),
-     // zeros past K; two loads' worth of row-chunks go out first
+     // zeros past K
     const uint32_t total = M * nchunk * 128u;
-    auto piece = [&](uint32_t x, u32x4_t &v, uint32_t &dst) {
+    auto piece = [&](uint32_t x, u32x4_t &v, uint32_t &dst) __attribute__((always_inline)) {
       const uint32_t m = x / (nchunk * 128u), rest = x - m * (nchunk * 128u);
       const uint32_t c = rest >> 7, p = rest & 127u;
       const uint32_t k = 1024u * c + 8u * p;
@@ -156,7 +167,6 @@ __global__ __launch_bounds__(kThreads) void w8a16_gemv_kernel(const uint16_t *__
       dst = m * a_pitch + kChunkBytes * c + 1024u * (p & 1u) + 16u * (p >> 1);
     };
     constexpr int UA = 4;
-    bool first = true;
     for (uint32_t base = 0; base < total; base += UA * kThreads) {
       u32x4_t v[UA];
       uint32_t dst[UA];
@@ -165,11 +175,6 @@ __global__ __launch_bounds__(kThreads) void w8a16_gemv_kernel(const uint16_t *__
         const uint32_t x = base + (uint32_t)u * kThreads + tid;
         if (x < total) piece(x, v[u], dst[u]);
       }
-      if (first) {
-        ring[0] = issue_next();
-        ring[1] = issue_next();
-        first = false;
-      }
 #pragma unroll
       for (int u = 0; u < UA; ++u) {
         const uint32_t x = base + (uint32_t)u * kThreads + tid;
@@ -177,20 +182,19 @@ __global__ __launch_bounds__(kThreads) void w8a16_gemv_kernel(const uint16_t *__
       }
     }
     __syncthreads();
-#pragma unroll
-    for (int d = 2; d < kDepth; ++d) ring[d] = issue_next();
+    unroll<0, DEPTH>([&](auto d) __attribute__((always_inline)) { ring[decltype(d)::value] = issue_next(); });
   }
 
-  float o[kRpw][MMAX];    // o_j of this lane's group j for row slot t, activation row m
+  float o[RPW][MMAX];    // o_j of this lane's group j for row slot t, activation row m
   uint32_t a[MMAX][8];    // this lane's 16 activations of the current chunk, as BF16 pairs
 #pragma unroll
-  for (int t = 0; t < kRpw; ++t)
+  for (int t = 0; t < RPW; ++t)
 #pragma unroll
     for (int m = 0; m < MMAX; ++m) o[t][m] = 0.0f;
 
   Cursor cc = {0u, 0u, 0u, 0u};
   // T: the row slot of this ring position (the ring is a whole number of groups' slots)
-  auto step = [&](ChunkRegs &r, auto T) {
+  auto step = [&](ChunkRegs &r, auto T) __attribute__((always_inline)) {
     constexpr int t = decltype(T)::value;
     const uint32_t c = cc.c, grp = cc.grp;
     if (t == 0) {
@@ -226,10 +230,10 @@ __global__ __launch_bounds__(kThreads) void w8a16_gemv_kernel(const uint16_t *__
       p = add_dpp<kDppHalfMirror>(p);
       o[t][m] = __fadd_rn(o[t][m], __fmul_rn(s, p));
     }
-    if (t == kRpw - 1 && c + 1u == nchunk) {  // the group's rows are complete
+    if (t == RPW - 1 && c + 1u == nchunk) {  // the group's rows are complete
 #pragma unroll
-      for (int tt = 0; tt < kRpw; ++tt) {
-        const uint32_t ti = grp * kRpw + tt;
+      for (int tt = 0; tt < RPW; ++tt) {
+        const uint32_t ti = grp * RPW + tt;
         const uint32_t n = r0 + wave + kWaves * ti;
 #pragma unroll
         for (int m = 0; m < MMAX; ++m) {
@@ -244,51 +248,55 @@ __global__ __launch_bounds__(kThreads) void w8a16_gemv_kernel(const uint16_t *__
     }
   };
 
-  while (cc.q + kDepth <= nq) {
-    step(ring[0], std::integral_constant<int, 0>{});
-    step(ring[1], std::integral_constant<int, 1>{});
-    step(ring[2], std::integral_constant<int, 2>{});
-    step(ring[3], std::integral_constant<int, 3>{});
-    step(ring[4], std::integral_constant<int, 0>{});
-    step(ring[5], std::integral_constant<int, 1>{});
-    step(ring[6], std::integral_constant<int, 2>{});
-    step(ring[7], std::integral_constant<int, 3>{});
-  }
-  if (cc.q < nq) {  // nq is a multiple of kRpw: one more whole group of slots
-    step(ring[0], std::integral_constant<int, 0>{});
-    step(ring[1], std::integral_constant<int, 1>{});
-    step(ring[2], std::integral_constant<int, 2>{});
-    step(ring[3], std::integral_constant<int, 3>{});
-  }
+  while (cc.q + DEPTH <= nq)
+    unroll<0, DEPTH>([&](auto d) __attribute__((always_inline)) {
+      constexpr int D = decltype(d)::value;
+      step(ring[D], std::integral_constant<int, D % RPW>{});
+    });
+  // the rest is a whole number of groups (nq is a multiple of RPW)
+  unroll<0, DEPTH>([&](auto d) __attribute__((always_inline)) {
+    constexpr int D = decltype(d)::value;
+    if (cc.q < nq) step(ring[D], std::integral_constant<int, D % RPW>{});
+  });
 }
-static_assert(kDepth == 8 && kRpw == 4, "the unrolled ring walk above assumes 8 slots of 4 rows");
 
+// Workgroups: one per CU, at least 8 rows (one per wave) each.
+uint32_t gemv_grid(uint32_t N, int cus) {
+  const uint32_t by_rows = (N + kWaves - 1u) / kWaves;
+  return by_rows < (uint32_t)cus ? by_rows : (uint32_t)cus;
+}
+
+template <int MMAX, int RPW>
+hipError_t launch_cfg(const void *A, const void *W, const float *S, void *C, uint32_t M, uint32_t N, uint32_t K,
+                      uint32_t lda, uint32_t ldc, size_t lds, uint32_t grid, hipStream_t stream) {
+  constexpr auto kern = w8a16_gemv_kernel<MMAX, RPW, 2 * RPW>;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, stream, static_cast<const uint16_t *>(A),
+                     static_cast<const uint8_t *>(W), S, static_cast<uint16_t *>(C), M, N, K, lda, ldc);
+  return hipGetLastError();
+}
+
+// Row groups as wide as a wave's share of rows, up to 3 (wider groups would
+// mostly pad: a wave holds N / (8 * CUs) rows, 2.5 for N = 5120 on 256 CUs),
+// with two groups' row-chunks in flight.
 template <int MMAX>
 hipError_t launch_mmax(const void *A, const void *W, const float *S, void *C, uint32_t M, uint32_t N, uint32_t K,
                        uint32_t lda, uint32_t ldc, size_t lds, hipStream_t stream) {
-  struct Res {
-    hipError_t err = hipSuccess;
-    int cus = 1;
-  };
-  static const Res res = [] {
-    Res r;
-    int dev = 0;
-    if ((r.err = hipFuncSetAttribute(reinterpret_cast<const void *>(&w8a16_gemv_kernel<MMAX>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024)) != hipSuccess)
-      return r;
-    if ((r.err = hipGetDevice(&dev)) != hipSuccess) return r;
-    if ((r.err = hipDeviceGetAttribute(&r.cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return r;
-    if (r.cus < 1) r.cus = 1;
-    return r;
-  }();
-  if (res.err != hipSuccess) return res.err;
-  // one workgroup per CU, at least 8 rows (one per wave) each
-  const uint32_t by_rows = (N + kWaves - 1u) / kWaves;
-  const uint32_t grid = by_rows < (uint32_t)res.cus ? by_rows : (uint32_t)res.cus;
-  hipLaunchKernelGGL(w8a16_gemv_kernel<MMAX>, dim3(grid), dim3(kThreads), lds, stream,
-                     static_cast<const uint16_t *>(A), static_cast<const uint8_t *>(W), S,
-                     static_cast<uint16_t *>(C), M, N, K, lda, ldc);
-  return hipGetLastError();
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    cus = n > 0 ? n : 1;
+  }
+  const uint32_t grid = gemv_grid(N, cus);
+  const uint32_t rows_per_wave = ((N + grid - 1u) / grid + kWaves - 1u) / kWaves;
+  if (rows_per_wave <= 1u) return launch_cfg<MMAX, 1>(A, W, S, C, M, N, K, lda, ldc, lds, grid, stream);
+  if (rows_per_wave <= 2u) return launch_cfg<MMAX, 2>(A, W, S, C, M, N, K, lda, ldc, lds, grid, stream);
+  return launch_cfg<MMAX, 3>(A, W, S, C, M, N, K, lda, ldc, lds, grid, stream);
 }
 
 }  // namespace
