@@ -118,6 +118,7 @@ class Q2Workload:
 
 class Fp8Workload:
     fmt = "w8a16"
+    entry = "w8a16_gemm_m16"  # the matrix-core GEMM; Fp8ValuWorkload times the vector-ALU GEMV
 
     def __init__(self, name, wid, N, K, M):
         self.name, self.wid, self.N, self.K, self.M = name, wid, N, K, M
@@ -139,9 +140,10 @@ class Fp8Workload:
 
     def call(self, wqd, i):
         W = self.ring[i % self.R]
+        fn = getattr(wqd, self.entry)
         for r0 in range(0, self.M, 16):  # 17..32 rows: two calls on contiguous halves
             rows = min(16, self.M - r0)
-            wqd.w8a16_gemm_m16(self.A[r0:r0 + rows], W, self.S, self.C[r0:r0 + rows], rows, self.N, self.K)
+            fn(self.A[r0:r0 + rows], W, self.S, self.C[r0:r0 + rows], rows, self.N, self.K)
 
     def check(self, torch, np, oracle, check_fn, copy_idx):
         A, W, S = self.host
@@ -162,6 +164,16 @@ class Fp8Workload:
         self.ring = self.A = self.C = self.S = None
 
 
+class Fp8ValuWorkload(Fp8Workload):
+    fmt = "w8a16-valu"
+    entry = "w8a16_gemv_batch16"
+
+    def __init__(self, name, wid, N, K, M):
+        super().__init__(name, wid, N, K, M)
+        rows = 8 if K <= 10240 else max(1, (160 * 1024) // (((K + 1023) // 1024) * 2048))  # rows per launch
+        self.dispatches = sum((min(16, M - r0) + rows - 1) // rows for r0 in range(0, M, 16))
+
+
 HEADLINE = ("q2_0 M=1 N=5120 K=5120", Q2Workload, 2, 5120, 5120, 1)
 
 
@@ -171,10 +183,13 @@ def sweep_list():
         out.append((f"q2_0 M={M} N=5120 K=5120", Q2Workload, 3, 5120, 5120, M))
     for M in (1, 8, 16):
         out.append((f"w8a16 M={M} N=5120 K=5120", Fp8Workload, 4, 5120, 5120, M))
+    for M in (1, 2, 4, 8):
+        out.append((f"w8a16-valu M={M} N=5120 K=5120", Fp8ValuWorkload, 4, 5120, 5120, M))
     for (N, K) in ((17408, 5120), (5120, 17408)):
         for M in (1, 8, 16, 32):
             out.append((f"q2_0 M={M} N={N} K={K}", Q2Workload, 5, N, K, M))
             out.append((f"w8a16 M={M} N={N} K={K}", Fp8Workload, 5, N, K, M))
+        out.append((f"w8a16-valu M=1 N={N} K={K}", Fp8ValuWorkload, 5, N, K, 1))
     return out
 
 

@@ -33,6 +33,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "wqd_internal.h"
 
 namespace wqd {
@@ -72,6 +74,15 @@ __device__ __forceinline__ bf16x8_t weights8(uint32_t lo4, uint32_t hi4) {
   v.z = fp8x2_to_bf16x2<false>(hi4);
   v.w = fp8x2_to_bf16x2<true>(hi4);
   return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// f(integral_constant<D>) for D = B .. E-1, unrolled at compile time
+template <int B, int E, typename F>
+__device__ __forceinline__ void unroll(F &&f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    unroll<B + 1, E>(f);
+  }
 }
 
 // Chunk slot s of a phase for this thread: slots 0-1 carry weight chunks (row
@@ -498,13 +509,146 @@ hipError_t launch_units_mmax(const void *A, const void *W, const float *S, void 
   return launch_units<w8a16_units_kernel<MMAX, 4, 10>>(lds, ntiles, band, stream, a, w, S, c, M, N, K, lda, ldc);
 }
 
+// ---------------------------------------------------------------------------
+// Register-resident-activation kernel (K up to 1024 * NBW): the same tiles,
+// block ownership, arithmetic and reduction order as the two kernels above,
+// so the same bits, but without staging the activations in LDS.
+//   * Wave w owns blocks w, w + 8, ... of every tile, and every tile needs the
+//     same activations for those blocks: lane (i, g) holds its 64 bytes of
+//     activation row i (row 0 for i >= M) for each of the wave's blocks in
+//     registers for the whole kernel (16 registers per block), read once from
+//     memory at the start.  Nothing limits M below 16 and no barrier
+//     precedes the first block.
+//   * The weights of the next tile's blocks are requested as the current
+//     tile's blocks are consumed (ring slot u serves the wave's u-th block of
+//     every tile); past the last tile the requests use an offset beyond the
+//     buffer, which fetches nothing.
+// ---------------------------------------------------------------------------
+template <int NBW>
+__global__ __launch_bounds__(kThreads) void w8a16_regs_kernel(const uint16_t *__restrict__ A,
+                                                              const uint8_t *__restrict__ W,
+                                                              const float *__restrict__ S,
+                                                              uint16_t *__restrict__ C, uint32_t M, uint32_t N,
+                                                              uint32_t K, uint32_t lda, uint32_t ldc,
+                                                              uint32_t band) {
+  constexpr int MMAX = 16;
+  using L = UnitLayout<MMAX>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const uint32_t tid = threadIdx.x;
+  const uint32_t lane = tid & 63u;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t i = lane & 15u, g = lane >> 4;
+  const uint32_t nb = K >> 7;
+  uint32_t r0, r1;  // rows of this workgroup, as in the kernel above
+  if (band == 0u) {
+    r0 = (uint32_t)(((uint64_t)N * blockIdx.x) / gridDim.x);
+    r1 = (uint32_t)(((uint64_t)N * (blockIdx.x + 1u)) / gridDim.x);
+  } else {
+    r0 = blockIdx.x * 16u * band;
+    r1 = min(r0 + 16u * band, N);
+  }
+  const uint32_t ntile = (r1 - r0 + 15u) >> 4;
+  const uint32_t upw = nb > wave ? (nb - wave + kWaves - 1u) / kWaves : 0u;  // <= NBW
+
+  const __amdgpu_buffer_rsrc_t wrsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(W), (short)0, (int)(N * K), 0x00020000);
+  const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float *>(S), (short)0, (int)(((N + 127u) >> 7) * nb * 4u), 0x00020000);
+  // block u of this wave in tile t (t = ntile: nothing)
+  auto issue = [&](uint32_t t, uint32_t u) __attribute__((always_inline)) {
+    const uint32_t b = min(wave + kWaves * u, nb - 1u);
+    const uint32_t row = r0 + 16u * t + i;
+    const bool ok = t < ntile && row < r1;
+    const uint32_t voff = ok ? row * K + 32u * g : kPastEnd;
+    const uint32_t srow = (ok ? row : r0) >> 7;
+    UnitRegs r;
+    r.w0 = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, voff, 128u * b, 0);
+    r.w1 = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, voff + 16u, 128u * b, 0);
+    r.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srsrc, ok ? srow * nb * 4u : kPastEnd,
+                                                                         4u * b, 0));
+    return r;
+  };
+
+  bf16x8_t a[NBW][4];
+  UnitRegs ring[NBW];
+  {
+    const uint16_t *arow = A + (size_t)(i < M ? i : 0u) * lda + 32u * g;
+    unroll<0, NBW>([&](auto uu) __attribute__((always_inline)) {
+      constexpr int u = decltype(uu)::value;
+      const uint32_t b = min(wave + kWaves * (uint32_t)u, nb - 1u);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[u][j] = *reinterpret_cast<const bf16x8_t *>(arow + 128u * b + 8u * j);
+    });
+    unroll<0, NBW>([&](auto uu) __attribute__((always_inline)) {
+      constexpr int u = decltype(uu)::value;
+      ring[u] = issue(0u, (uint32_t)u);
+    });
+  }
+
+  float *part = reinterpret_cast<float *>(lds + L::kPart);
+  for (uint32_t t = 0; t < ntile; ++t) {
+    f32x4_t outer = {0.0f, 0.0f, 0.0f, 0.0f};
+    unroll<0, NBW>([&](auto uu) __attribute__((always_inline)) {
+      constexpr int u = decltype(uu)::value;
+      if ((uint32_t)u < upw) {
+        const UnitRegs r = ring[u];
+        ring[u] = issue(t + 1u, (uint32_t)u);
+        f32x4_t x = {0.0f, 0.0f, 0.0f, 0.0f};
+        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][0], weights8(r.w0.x, r.w0.y), x, 0, 0, 0);
+        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][1], weights8(r.w0.z, r.w0.w), x, 0, 0, 0);
+        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][2], weights8(r.w1.x, r.w1.y), x, 0, 0, 0);
+        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][3], weights8(r.w1.z, r.w1.w), x, 0, 0, 0);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) outer[rr] = __fadd_rn(outer[rr], __fmul_rn(r.s, x[rr]));
+      }
+    });
+    // the 8 waves' partial tiles, added in wave order (tile parity alternates
+    // the buffer, so one barrier per tile suffices)
+    const uint32_t par = t & 1u;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const uint32_t m = 4u * g + rr;
+      if (m < M) part[((par * kWaves + wave) * MMAX + m) * 16u + i] = outer[rr];
+    }
+    __syncthreads();
+    if (tid < M * 16u) {
+      const uint32_t m = tid >> 4, col = tid & 15u;
+      const uint32_t n = r0 + 16u * t + col;
+      if (n < r1) {
+        const float *pp = part + (par * kWaves * MMAX + m) * 16u + col;
+        float v = pp[0];
+        for (uint32_t w = 1; w < kWaves; ++w) v = v + pp[w * MMAX * 16u];
+        C[(size_t)m * ldc + n] = f32_to_bf16_rne(v);
+      }
+    }
+  }
+}
+
+template <int NBW>
+hipError_t launch_regs(const void *A, const void *W, const float *S, void *C, uint32_t M, uint32_t N, uint32_t K,
+                       uint32_t lda, uint32_t ldc, uint32_t band, hipStream_t stream) {
+  return launch_units<w8a16_regs_kernel<NBW>>((size_t)UnitLayout<16>::kA, (N + 15u) / 16u, band, stream,
+                                              static_cast<const uint16_t *>(A), static_cast<const uint8_t *>(W), S,
+                                              static_cast<uint16_t *>(C), M, N, K, lda, ldc);
+}
+
 }  // namespace
 
 hipError_t launch_w8a16_m16(const void *A, const void *W, const float *S, void *C, uint32_t M, uint32_t N,
                             uint32_t K, uint32_t lda, uint32_t ldc, uint32_t band, hipStream_t stream) {
-  // the resident-activation kernel when A fits in LDS and the weights in one
-  // buffer range; the per-phase kernel otherwise (same bits either way)
+  // every kernel gives the same bits; the choice is by speed and by what fits
   const bool bounded = (uint64_t)N * K < (1ull << 31);
+  const uint32_t nbw = ((K >> 7) + kWaves - 1u) / kWaves;  // blocks per wave and tile
+  // 9..16 rows with up to 5 blocks per wave (K <= 5120): activations in
+  // registers (measured on MI355X at N = K = 5120, M = 16: 12.7 us against
+  // 16.2 us per phase).  Up to 8 rows the LDS copy is cheaper: each wave
+  // would otherwise fetch its own copy of the activations.
+  if (bounded && M > 8 && nbw <= 5u) {
+    if (nbw <= 1u) return launch_regs<1>(A, W, S, C, M, N, K, lda, ldc, band, stream);
+    if (nbw <= 2u) return launch_regs<2>(A, W, S, C, M, N, K, lda, ldc, band, stream);
+    if (nbw <= 4u) return launch_regs<4>(A, W, S, C, M, N, K, lda, ldc, band, stream);
+    return launch_regs<5>(A, W, S, C, M, N, K, lda, ldc, band, stream);
+  }
   if (bounded && M <= 8 && unit_lds_bytes<8>(M, K) <= 160u * 1024u) {
     if (M <= 1) return launch_units_mmax<1>(A, W, S, C, M, N, K, lda, ldc, band, stream);
     if (M <= 2) return launch_units_mmax<2>(A, W, S, C, M, N, K, lda, ldc, band, stream);
