@@ -145,3 +145,18 @@ def test_ffn_shapes(oracle_mod, N, K):
     cols = np.sort(gen.rng(905, N, K).choice(N, 512, replace=False))
     ref = oracle_mod.q2_0_gemv(A, codes[cols], d[cols])
     check_parity(got32[:, cols], ref, f"q2_0 {N}x{K} M=32 sampled")
+
+
+@pytest.mark.parametrize("N,K,M", [(37, 12288, 8), (200, 12288, 7), (1, 12288, 8), (333, 17408, 6), (2049, 10240, 8)])
+def test_large_k_batched_rows(oracle_mod, N, K, M):
+    """Activations too large for LDS (the per-phase kernel with super-tiles of
+    up to four 8-row tiles over an even row split): ragged N, every row
+    bit-identical to its own M=1 launch (the resident-activation kernel) and
+    within tolerance of the oracle on a column sample."""
+    A, codes, d, packed = _case(31, N, K, M, salt=N + K)
+    Bd = dev_u8(packed)
+    got = q2_0_gpu(A, Bd, N, K)
+    for m in range(M):
+        assert np.array_equal(got[m:m + 1], q2_0_gpu(A[m:m + 1], Bd, N, K, single=True)), m
+    cols = np.arange(N) if N <= 400 else np.sort(gen.rng(931, N, K).choice(N, 256, replace=False))
+    check_parity(got[:, cols], oracle_mod.q2_0_gemv(A, codes[cols], d[cols]), f"q2_0 {N}x{K} M={M}")

@@ -131,74 +131,85 @@ __device__ __forceinline__ f32x4_t neg_sum_chain(const bf16x8_t (&a)[4]) {
 // ---------------------------------------------------------------------------
 // Per-phase kernel: for activations too large to keep in LDS.  Same unit
 // assignment, seeds, chains and reduction order as the pairs kernel below, so
-// both give the same bits.  A workgroup walks its tiles in phases of 16
-// blocks: each phase's 8 x 544 weight bytes and 16 blocks of every activation
-// row are fetched with 16-byte loads in which consecutive lanes read
-// consecutive addresses, kept DEPTH phases ahead in registers and written to
-// one of two LDS buffers (one barrier per phase); wave w computes block pair
-// w of the phase (pair 8p + w of the tile) with its seed computed in line.
+// both give the same bits.  One workgroup per CU owns an even share [r0, r1)
+// of the weight rows and walks it in super-tiles of TPP 8-row tiles (rows past
+// r1 re-read row r1 - 1 and are never stored), each in phases of 16 blocks:
+// a phase's TPP x 8 x 544 weight bytes and 16 blocks of every activation row
+// are fetched with 16-byte loads in which consecutive lanes read consecutive
+// addresses, kept DEPTH phases ahead in registers and written to one of two
+// LDS buffers (one barrier per phase).  Wave w computes block pair w of the
+// phase for every tile of the super-tile: the activations and their seed are
+// read and computed once and serve all TPP tiles, so the activation traffic
+// per weight row falls by TPP.
 // ---------------------------------------------------------------------------
-// LDS: [buffer 0][buffer 1][zero rows: 256][partial tiles: 2 x kWaves x 2 x
-// MMAX x 8 floats].  A buffer holds the phase's weight rows, MMAX
+// LDS: [buffer 0][buffer 1][zero rows: 256][partial tiles: 2 x TPP x kWaves x
+// 2 x MMAX x 8 floats].  A buffer holds the phase's TPP x 8 weight rows, MMAX
 // activation-row segments and a 16-byte dummy slot at kDummy
 // (buffer-relative).
-template <int MMAX>
+template <int MMAX, int TPP>
 struct PhaseLayout {
-  static constexpr int kSlots = 1 + (MMAX * (kAPhaseBytes / 16) + kThreads - 1) / kThreads;
-  static constexpr int kDummy = kWBytes + MMAX * kAPitch;
+  static constexpr int kWRows = TPP * kRows;
+  static constexpr int kWSlots = (kWRows * (kPhaseRowBytes / 16) + kThreads - 1) / kThreads;
+  static constexpr int kSlots = kWSlots + (MMAX * (kAPhaseBytes / 16) + kThreads - 1) / kThreads;
+  static constexpr int kWBytesT = kWRows * kWPitch;
+  static constexpr int kDummy = kWBytesT + MMAX * kAPitch;
   static constexpr int kBuf = kDummy + 16;
   static constexpr int kZero = 2 * kBuf;
   static constexpr int kPart = kZero + 256;
-  static constexpr int kFixed = kPart + 2 * kWaves * 2 * MMAX * kRows * 4;
+  static constexpr int kFixed = kPart + 2 * TPP * kWaves * 2 * MMAX * kRows * 4;
 };
 
-// The 16-byte chunk slots of a thread.  Slot 0 carries weight chunks: row
-// r = tid / c of the tile, column tid % c of the row's phase segment, c = 34
-// chunks in a full phase (17 in a half-length last phase).  Slots 1.. carry
-// per-phase activation chunks: k = (s-1)*512 + tid, row m = k/256, column
-// k%256.  Every slot keeps two precomputed (source offset, LDS destination)
-// pairs: one for full phases and one for the K tail's phase.  A chunk with
-// nothing to fetch re-reads an in-bounds chunk and goes to the dummy LDS slot.
-// For N < 8 a row past N re-reads row N - 1 and its outputs are never stored.
+// The 16-byte chunk slots of a thread.  Slots 0 .. WS-1 carry weight chunks:
+// chunk c = s * 512 + tid is row c / w of the super-tile, column c % w of the
+// row's phase segment (w = 34 chunks in a full phase, 17 in a half-length last
+// phase); its source row is resolved per super-tile.  Slots WS.. carry
+// per-phase activation chunks: k = (s - WS) * 512 + tid, row m = k / 256,
+// column k % 256.  Every slot keeps two precomputed variants: one for full
+// phases and one for the K tail's phase.  A chunk with nothing to fetch
+// re-reads an in-bounds chunk and goes to the dummy LDS slot.
 template <int S>
 struct Slots {
-  uint32_t src[2][S];  // [full, tail]
+  uint32_t src[2][S];  // weight slots: (row in super-tile) << 16 | byte column, or kNoRow; activation slots: offset
   uint32_t dst[2][S];
 };
+constexpr uint32_t kNoRow = 0xFFFFFFFFu;
 
-template <int S>
-__device__ __forceinline__ void make_slots(Slots<S> &sl, uint32_t tid, uint32_t N, uint32_t rb, uint32_t K,
-                                           uint32_t M, uint32_t tail_blocks, uint32_t dummy) {
+template <int S, int WS, int WROWS>
+__device__ __forceinline__ void make_slots(Slots<S> &sl, uint32_t tid, uint32_t K, uint32_t M,
+                                           uint32_t tail_blocks, uint32_t dummy) {
 #pragma unroll
   for (int v = 0; v < 2; ++v) {
     const uint32_t pbn = v == 0 ? (uint32_t)kPhaseBlocks : tail_blocks;
     const uint32_t wcols = pbn * kBlockBytes / 16u, acols = pbn * 16u;
-    {
-      const uint32_t r = tid / wcols, col = tid - r * wcols;
-      const bool in = r < (uint32_t)kRows;
-      const uint32_t row = in ? min(r, N - 1u) : 0u;
-      sl.src[v][0] = in ? row * rb + 16u * col : 0u;
-      sl.dst[v][0] = in ? r * kWPitch + 16u * col : dummy;
+#pragma unroll
+    for (int s = 0; s < WS; ++s) {
+      const uint32_t c = (uint32_t)s * kThreads + tid;
+      const uint32_t r = c / wcols, col = c - r * wcols;
+      const bool in = r < (uint32_t)WROWS;
+      sl.src[v][s] = in ? (r << 16) | (16u * col) : kNoRow;
+      sl.dst[v][s] = in ? r * kWPitch + 16u * col : dummy;
     }
 #pragma unroll
-    for (int s = 1; s < S; ++s) {
-      const uint32_t c = (uint32_t)(s - 1) * kThreads + tid;
+    for (int s = WS; s < S; ++s) {
+      const uint32_t c = (uint32_t)(s - WS) * kThreads + tid;
       const uint32_t m = c >> 8, col = c & 255u;
       const bool in = m < M && col < acols;
       sl.src[v][s] = in ? m * K * 2u + 16u * col : 0u;
-      sl.dst[v][s] = in ? kWBytes + m * kAPitch + 16u * col : dummy;
+      sl.dst[v][s] = in ? (uint32_t)(WROWS * kWPitch) + m * kAPitch + 16u * col : dummy;
     }
   }
 }
 
-template <int MMAX, int DEPTH>
+template <int MMAX, int DEPTH, int TPP>
 __global__ __launch_bounds__(kThreads) void q2_0_phase_kernel(const uint16_t *__restrict__ A,
                                                               const uint8_t *__restrict__ B,
                                                               uint16_t *__restrict__ C, uint32_t N, uint32_t K,
                                                               uint32_t M) {
-  using L = PhaseLayout<MMAX>;
+  using L = PhaseLayout<MMAX, TPP>;
   constexpr int S = L::kSlots;
-  constexpr int NF = MMAX < 4 ? MMAX : 4;  // accumulator rows that can hold outputs
+  constexpr int WS = L::kWSlots;
+  constexpr uint32_t kSpan = (uint32_t)L::kWRows;  // rows per super-tile
+  constexpr int NF = MMAX < 4 ? MMAX : 4;          // accumulator rows that can hold outputs
   static_assert(DEPTH % 2 == 0, "buffer parity must be a compile-time function of the ring slot");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const uint32_t tid = threadIdx.x;
@@ -209,12 +220,13 @@ __global__ __launch_bounds__(kThreads) void q2_0_phase_kernel(const uint16_t *__
   const uint32_t nb = K >> 7;
   const uint32_t nphase = (nb + kPhaseBlocks - 1) / kPhaseBlocks;
   const uint32_t tail_blocks = nb - (nphase - 1u) * kPhaseBlocks;  // 8 or 16
-  const uint32_t rb = nb * kBlockBytes;
-  const uint32_t ntiles = N >= (uint32_t)kRows ? (N + kRows - 1u) / kRows : 1u;
-  // This workgroup's tiles are blockIdx.x, blockIdx.x + gridDim.x, ...; its
-  // phases form one sequence over them, and the load ring runs across tile
-  // boundaries so the next tile's first phases are in flight when a tile ends.
-  const uint32_t my_tiles = (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x;
+  const size_t rb = (size_t)nb * kBlockBytes;
+  const uint32_t r0 = (uint32_t)(((uint64_t)N * blockIdx.x) / gridDim.x);
+  const uint32_t r1 = (uint32_t)(((uint64_t)N * (blockIdx.x + 1u)) / gridDim.x);
+  // This workgroup's super-tiles start at r0, r0 + kSpan, ...; its phases
+  // form one sequence over them, and the load ring runs across super-tile
+  // boundaries so the next one's first phases are in flight when one ends.
+  const uint32_t my_tiles = (r1 - r0 + kSpan - 1u) / kSpan;
   const uint32_t nq = my_tiles * nphase;
 
   // zero region standing in for activation rows m >= M
@@ -224,75 +236,85 @@ __global__ __launch_bounds__(kThreads) void q2_0_phase_kernel(const uint16_t *__
   }
 
   Slots<S> sl;
-  make_slots<S>(sl, tid, N, rb, K, M, tail_blocks, L::kDummy);
-  auto tile_row = [&](uint32_t j) {
-    const uint32_t n0 = (blockIdx.x + j * gridDim.x) * (uint32_t)kRows;
-    return N >= (uint32_t)kRows ? min(n0, N - (uint32_t)kRows) : 0u;
-  };
+  make_slots<S, WS, (int)kSpan>(sl, tid, K, M, tail_blocks, L::kDummy);
 
-  // Sequence element q is phase q % nphase of this workgroup's tile q / nphase.
-  // Past the end (q >= nq) it re-reads phase 0 of the first tile, stored nowhere.
-  auto issue_q = [&](uint32_t q, u32x4_t(&r)[S]) {
+  // Sequence element q is phase q % nphase of this workgroup's super-tile
+  // q / nphase.  Past the end (q >= nq) it re-reads phase 0 of the first one,
+  // stored nowhere.
+  auto issue_q = [&](uint32_t q, u32x4_t(&r)[S]) __attribute__((always_inline)) {
     const bool live = q < nq;
     const uint32_t j = live ? q / nphase : 0u;
     const uint32_t p = live ? q - j * nphase : 0u;
     const bool tail = p + 1u == nphase;
-    const uint8_t *wb = B + (size_t)tile_row(j) * rb + (size_t)p * kPhaseRowBytes;
+    const uint32_t base = r0 + j * kSpan;
     const uint8_t *ab = reinterpret_cast<const uint8_t *>(A) + (size_t)p * kAPhaseBytes;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-      const uint32_t off = tail ? sl.src[1][s] : sl.src[0][s];
-      r[s] = *reinterpret_cast<const u32x4_t *>((s == 0 ? wb : ab) + off);
+      const uint32_t v = tail ? sl.src[1][s] : sl.src[0][s];
+      if (s < WS) {
+        const uint32_t row = v == kNoRow ? r0 : min(base + (v >> 16), r1 - 1u);
+        const uint32_t col = v == kNoRow ? 0u : (v & 0xFFFFu);
+        r[s] = *reinterpret_cast<const u32x4_t *>(B + (size_t)row * rb + (size_t)p * kPhaseRowBytes + col);
+      } else {
+        r[s] = *reinterpret_cast<const u32x4_t *>(ab + v);
+      }
     }
   };
 
   // This lane's MFMA operands within a phase: weight row rw of block 2*wave+h
-  // (its fp16 scale at wblk; its 8 code bytes inside the aligned 3-dword
-  // window at wwin, which `sel` extracts), and activation row rw of the same
-  // block (or the zero region).
+  // of tile t (its fp16 scale at wblk; its 8 code bytes inside the aligned
+  // 3-dword window at wwin, which `sel` extracts; + t * 8 rows), and
+  // activation row rw of the same block (or the zero region).
   const uint32_t wblk = rw * kWPitch + 34u * h + 68u * wave;
   const uint32_t wwin = rw * kWPitch + 32u * h + 8u * g + 68u * wave;  // code bytes at +2 (h = 0) or +4 (h = 1)
   const uint32_t sel = h ? 0x07060504u : 0x05040302u;
   const bool a_ok = rw < M;
-  const uint32_t a_lane =
-      a_ok ? (uint32_t)kWBytes + rw * kAPitch + (2u * wave + h) * 256u + 64u * g : (uint32_t)L::kZero + 64u * g;
+  const uint32_t a_lane = a_ok ? (uint32_t)L::kWBytesT + rw * kAPitch + (2u * wave + h) * 256u + 64u * g
+                               : (uint32_t)L::kZero + 64u * g;
   const uint32_t a_buf = a_ok ? (uint32_t)L::kBuf : 0u;  // + per buffer
   const bool lane_out = (g >> 1) == h;  // this lane's accumulator rows match its column's block half
-  float *part = reinterpret_cast<float *>(lds + L::kPart);  // [tile parity][wave][half][m][r]
+  float *part = reinterpret_cast<float *>(lds + L::kPart);  // [parity][tile][wave][half][m][r]
 
   u32x4_t ring[DEPTH][S];
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d) issue_q((uint32_t)d, ring[d]);
 
-  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  // The wave's block pair of the phase in buffer `parity` into acc.
-  auto unit = [&](uint32_t parity) {
+  f32x4_t acc[TPP];
+#pragma unroll
+  for (int t = 0; t < TPP; ++t) acc[t] = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
+  // The wave's block pair of the phase in buffer `parity`, for every tile.
+  auto unit = [&](uint32_t parity) __attribute__((always_inline)) {
     const uint8_t *buf = lds + parity * L::kBuf;
     const uint8_t *act = lds + a_lane + parity * a_buf;
     bf16x8_t a[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) a[j] = *reinterpret_cast<const bf16x8_t *>(act + 16 * j);
-    f32x4_t x = neg_sum_chain(a);
-    const uint32_t *pw = reinterpret_cast<const uint32_t *>(buf + wwin);
-    const uint32_t c0 = pw[0], c1 = pw[1], c2 = pw[2];
-    const uint32_t w0 = __builtin_amdgcn_perm(c1, c0, sel);
-    const uint32_t w1 = __builtin_amdgcn_perm(c2, c1, sel);
-    const _Float16 d = *reinterpret_cast<const _Float16 *>(buf + wblk);
-    bf16x8_t b0, b1, b2, b3;
-    decode_word(w0, b0, b1);
-    decode_word(w1, b2, b3);
-    x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b0, x, 0, 0, 0);
-    x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], b1, x, 0, 0, 0);
-    x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2], b2, x, 0, 0, 0);
-    x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[3], b3, x, 0, 0, 0);
+    const f32x4_t seed = neg_sum_chain(a);
 #pragma unroll
-    for (int r = 0; r < NF; ++r) acc[r] = __builtin_fmaf((float)d, x[r], acc[r]);
+    for (int t = 0; t < TPP; ++t) {
+      const uint8_t *tb = buf + t * (kRows * kWPitch);
+      const uint32_t *pw = reinterpret_cast<const uint32_t *>(tb + wwin);
+      const uint32_t c0 = pw[0], c1 = pw[1], c2 = pw[2];
+      const uint32_t w0 = __builtin_amdgcn_perm(c1, c0, sel);
+      const uint32_t w1 = __builtin_amdgcn_perm(c2, c1, sel);
+      const _Float16 d = *reinterpret_cast<const _Float16 *>(tb + wblk);
+      bf16x8_t b0, b1, b2, b3;
+      decode_word(w0, b0, b1);
+      decode_word(w1, b2, b3);
+      f32x4_t x = seed;
+      x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b0, x, 0, 0, 0);
+      x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], b1, x, 0, 0, 0);
+      x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2], b2, x, 0, 0, 0);
+      x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[3], b3, x, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < NF; ++r) acc[t][r] = __builtin_fmaf((float)d, x[r], acc[t][r]);
+    }
   };
 
   // One sequence element: store its chunks into buffer `parity`, request the
-  // element DEPTH ahead into the same registers, compute, and finish the tile
-  // after its last phase.
-  auto step = [&](uint32_t q, uint32_t parity, u32x4_t(&r)[S]) {
+  // element DEPTH ahead into the same registers, compute, and finish the
+  // super-tile after its last phase.
+  auto step = [&](uint32_t q, uint32_t parity, u32x4_t(&r)[S]) __attribute__((always_inline)) {
     uint8_t *buf = lds + parity * L::kBuf;
     const uint32_t j = q / nphase, p = q - j * nphase;
     const bool tail = p + 1u == nphase;
@@ -300,33 +322,39 @@ __global__ __launch_bounds__(kThreads) void q2_0_phase_kernel(const uint16_t *__
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       const uint32_t dst = tail ? sl.dst[1][s] : sl.dst[0][s];
-      *reinterpret_cast<u32x4_t *>(buf + dst) = s == 0 ? r[s] : permute_acts(r[s]);
+      *reinterpret_cast<u32x4_t *>(buf + dst) = s < WS ? r[s] : permute_acts(r[s]);
     }
     issue_q(q + DEPTH, r);
     __syncthreads();
     if (wave < npairs) unit(parity);
-    if (tail) {  // tile done: add the 16 partial sums of each output in fixed order
+    if (tail) {  // super-tile done: add the 16 partial sums of each output in fixed order
       const uint32_t par = j & 1u;
       if (lane_out) {
 #pragma unroll
-        for (int rr = 0; rr < NF; ++rr) {
-          const uint32_t m = 4u * (g & 1u) + rr;
-          if (m < M) part[(((par * kWaves + wave) * 2u + h) * MMAX + m) * kRows + rw] = acc[rr];
+        for (int t = 0; t < TPP; ++t) {
+#pragma unroll
+          for (int rr = 0; rr < NF; ++rr) {
+            const uint32_t m = 4u * (g & 1u) + rr;
+            if (m < M)
+              part[((((par * TPP + t) * kWaves + wave) * 2u + h) * MMAX + m) * kRows + rw] = acc[t][rr];
+          }
         }
       }
-      acc = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int t = 0; t < TPP; ++t) acc[t] = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
       __syncthreads();
-      if (tid < M * (uint32_t)kRows) {
-        const uint32_t m = tid >> 3, col = tid & 7u;
-        const uint32_t n = tile_row(j) + col;
-        if (n < N) {
-          const float *pp = part + (par * kWaves * 2u * MMAX + m) * kRows + col;
+      if (tid < M * kSpan) {
+        const uint32_t m = tid / kSpan, col = tid - m * kSpan;
+        const uint32_t t = col >> 3, r = col & 7u;
+        const uint32_t n = r0 + j * kSpan + col;
+        if (n < r1) {
+          const float *pp = part + ((par * TPP + t) * kWaves * 2u * MMAX + m) * kRows + r;
           float v = pp[0];
           for (uint32_t k = 1; k < 2u * kWaves; ++k) v = v + pp[k * MMAX * kRows];
           C[(size_t)m * N + n] = f32_to_bf16_rne(v);
         }
       }
-      // the next write of this parity's partials comes after another tile's barriers
+      // the next write of this parity's partials comes after another super-tile's barriers
     }
   };
 
@@ -339,7 +367,6 @@ __global__ __launch_bounds__(kThreads) void q2_0_phase_kernel(const uint16_t *__
   for (int d = 0; d < DEPTH; ++d)
     if (q + d < nq) step(q + d, (uint32_t)(d & 1), ring[d]);
 }
-
 
 // ---------------------------------------------------------------------------
 // Resident-activation kernel (the usual case): per-wave block pairs.
@@ -605,6 +632,45 @@ hipError_t launch_persistent(int threads, size_t lds, uint32_t ntiles, hipStream
   return hipGetLastError();
 }
 
+template <int MMAX, int TPP>
+hipError_t launch_phase_tpp(uint32_t grid, hipStream_t stream, const uint16_t *a, const uint8_t *b, uint16_t *c,
+                            uint32_t N, uint32_t K, uint32_t M) {
+  constexpr auto kern = q2_0_phase_kernel<MMAX, 2, TPP>;
+  constexpr size_t lds = PhaseLayout<MMAX, TPP>::kFixed;
+  static_assert(lds <= kLdsMax, "per-phase kernel exceeds LDS");
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, stream, a, b, c, N, K, M);
+  return hipGetLastError();
+}
+
+// One workgroup per CU (one needs up to 135 KB of LDS at 8 rows), the rows
+// split evenly; super-tiles as wide as the share of rows needs, up to 4
+// tiles (32 rows), so every CU streams the same bytes and fetches the
+// activations once per super-tile.
+template <int MMAX>
+hipError_t launch_phase(const uint16_t *a, const uint8_t *b, uint16_t *c, uint32_t N, uint32_t K, uint32_t M,
+                        hipStream_t stream) {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    cus = n > 0 ? n : 1;
+  }
+  const uint32_t ntiles = (N + kRows - 1u) / kRows;
+  const uint32_t grid = ntiles < (uint32_t)cus ? ntiles : (uint32_t)cus;
+  const uint32_t rows = (N + grid - 1u) / grid;
+  const uint32_t nsuper = (rows + 4u * kRows - 1u) / (4u * kRows);
+  const uint32_t tpp = (rows + kRows * nsuper - 1u) / (kRows * nsuper);
+  if (tpp <= 1u) return launch_phase_tpp<MMAX, 1>(grid, stream, a, b, c, N, K, M);
+  if (tpp <= 2u) return launch_phase_tpp<MMAX, 2>(grid, stream, a, b, c, N, K, M);
+  if (tpp <= 3u) return launch_phase_tpp<MMAX, 3>(grid, stream, a, b, c, N, K, M);
+  return launch_phase_tpp<MMAX, 4>(grid, stream, a, b, c, N, K, M);
+}
+
 template <int MMAX>
 hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32_t K, uint32_t M,
                        hipStream_t stream) {
@@ -625,8 +691,7 @@ hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32
     return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 10>>(64 * NW, lds, ntiles, stream, a, b, c, N, K, M);
   }
   // else per phase (same bits)
-  return launch_persistent<q2_0_phase_kernel<MMAX, 2>>(kThreads, PhaseLayout<MMAX>::kFixed, ntiles, stream, a, b, c,
-                                                       N, K, M);
+  return launch_phase<MMAX>(a, b, c, N, K, M, stream);
 }
 
 }  // namespace
