@@ -398,7 +398,7 @@ struct PairRegs {
 // Weight bytes go straight from memory to the lanes that use them (buffer
 // loads bounded by the matrix size): lane (h, r, g) reads 12 bytes at
 // 68p + 32h + 8g of weight row r and 2 bytes (the scale) at 68p + 34h.
-template <int MMAX, int NW, int DEPTH, int UA>
+template <int MMAX, int NW, int DEPTH, int UA, bool WFIRST>
 __global__ __launch_bounds__(64 * NW) void q2_0_pairs_kernel(const uint16_t *__restrict__ A,
                                                              const uint8_t *__restrict__ B,
                                                              uint16_t *__restrict__ C, uint32_t N, uint32_t K,
@@ -502,9 +502,19 @@ __global__ __launch_bounds__(64 * NW) void q2_0_pairs_kernel(const uint16_t *__r
 #pragma unroll
       for (int u = 0; u < U; ++u) *reinterpret_cast<u32x4_t *>(lds + adst[u]) = permute_acts(av[u]);
     };
-    a_load(0u);
+    // WFIRST: the first pairs' weights are requested before the activations
+    // (faster for large matrices and batched rows); otherwise after them
+    // (faster for one row of a small matrix, where the activation copy is on
+    // the critical path)
+    if constexpr (WFIRST) {
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d) ring[d] = issue_next();
+      for (int d = 0; d < DEPTH; ++d) ring[d] = issue_next();
+    }
+    a_load(0u);
+    if constexpr (!WFIRST) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) ring[d] = issue_next();
+    }
     a_store();
     for (uint32_t base = U * (64u * NW); base < total; base += U * (64u * NW)) {
       a_load(base);
@@ -684,11 +694,25 @@ hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32
   if (lds <= kLdsMax && bounded) {  // activations fit in LDS: the pairs kernel
     // activation chunks per thread for one staging round covering all of A
     const uint32_t per_thread = (M * (K >> 3) + 64 * NW - 1) / (64 * NW);
+    // measured on MI355X: activations first only pays for one row of a
+    // matrix under 16 MB (N = K = 5120, M = 1: 5.55 against 5.72 us; weights
+    // first: N = 17408, K = 5120, M = 1 9.7 against 10.4 us, M = 8 at
+    // N = K = 5120 6.8 against 7.0 us)
+    const bool wfirst = M > 1 || (uint64_t)N * (K >> 7) * kBlockBytes >= (16ull << 20);
+    if (!wfirst) {
+      if constexpr (MMAX == 1) {
+        if (per_thread <= 2)
+          return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 2, false>>(64 * NW, lds, ntiles, stream, a, b, c, N, K, M);
+        if (per_thread <= 4)
+          return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 4, false>>(64 * NW, lds, ntiles, stream, a, b, c, N, K, M);
+        return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 10, false>>(64 * NW, lds, ntiles, stream, a, b, c, N, K, M);
+      }
+    }
     if (per_thread <= 2)
-      return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 2>>(64 * NW, lds, ntiles, stream, a, b, c, N, K, M);
+      return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 2, true>>(64 * NW, lds, ntiles, stream, a, b, c, N, K, M);
     if (per_thread <= 4)
-      return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 4>>(64 * NW, lds, ntiles, stream, a, b, c, N, K, M);
-    return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 10>>(64 * NW, lds, ntiles, stream, a, b, c, N, K, M);
+      return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 4, true>>(64 * NW, lds, ntiles, stream, a, b, c, N, K, M);
+    return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 10, true>>(64 * NW, lds, ntiles, stream, a, b, c, N, K, M);
   }
   // else per phase (same bits)
   return launch_phase<MMAX>(a, b, c, N, K, M, stream);
