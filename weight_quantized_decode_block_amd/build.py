@@ -20,6 +20,8 @@ HIPCC_FLAGS = [
     "-ffp-contract=off",
     # packed fp32 VALU forms are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # kernel arguments preloaded into SGPRs at dispatch (no scalar load before the first instruction)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 

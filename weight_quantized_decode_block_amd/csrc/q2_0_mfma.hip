@@ -483,19 +483,23 @@ __global__ __launch_bounds__(64 * NW) void q2_0_pairs_kernel(const uint16_t *__r
     // usually holds all of A; later rounds wait behind the ring's loads
     const uint32_t cpr = K >> 3;
     const uint32_t total = M * cpr;
-    const uint32_t spare = tid % total;  // in-bounds chunk re-read by idle slots
     constexpr int U = UA;
     u32x4_t av[U];
     uint32_t adst[U];
+    // Chunk c of A (16 bytes, row c / cpr) goes to LDS byte a_off + 16 * (c + row):
+    // rows are 2K + 16 bytes apart.  The row is counted with MMAX - 1 compares
+    // (no division).  Idle slots re-read chunk 0 and write into the partials.
     auto a_load = [&](uint32_t base) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const uint32_t c = base + (uint32_t)u * (64u * NW) + tid;
         const bool in = c < total;
-        const uint32_t cc = in ? c : spare;
-        const uint32_t m = cc / cpr, col = cc - m * cpr;
+        const uint32_t cc = in ? c : 0u;
+        uint32_t m = 0;
+#pragma unroll
+        for (int j = 1; j < MMAX; ++j) m += cc >= (uint32_t)j * cpr ? 1u : 0u;
         av[u] = *reinterpret_cast<const u32x4_t *>(reinterpret_cast<const uint8_t *>(A) + (size_t)cc * 16u);
-        adst[u] = in ? a_off + m * a_pitch + 16u * col : (uint32_t)L::kPart;  // idle: into the partials
+        adst[u] = in ? a_off + 16u * (cc + m) : (uint32_t)L::kPart;
       }
     };
     auto a_store = [&]() {
