@@ -615,11 +615,12 @@ __global__ __launch_bounds__(64 * NW) void q2_0_pairs_kernel(const uint16_t *__r
 }
 
 // Launches KERN as a persistent grid: as many workgroups as fit on the device
-// at once, by registers (resolved once per kernel and process) and by LDS
-// (per call), each walking every gridDim.x-th tile.
+// at once, by registers (resolved once per kernel and process), by LDS (per
+// call) and at most max_per_cu per compute unit, each walking every
+// gridDim.x-th tile.
 template <auto KERN>
-hipError_t launch_persistent(int threads, size_t lds, uint32_t ntiles, hipStream_t stream, const uint16_t *a,
-                             const uint8_t *b, uint16_t *c, uint32_t N, uint32_t K, uint32_t M) {
+hipError_t launch_persistent(int threads, size_t lds, int max_per_cu, uint32_t ntiles, hipStream_t stream,
+                             const uint16_t *a, const uint8_t *b, uint16_t *c, uint32_t N, uint32_t K, uint32_t M) {
   struct Res {
     hipError_t err = hipSuccess;
     int wg_per_cu = 1, cus = 1;
@@ -639,7 +640,8 @@ hipError_t launch_persistent(int threads, size_t lds, uint32_t ntiles, hipStream
   }();
   if (res.err != hipSuccess) return res.err;
   const int by_lds = (int)(kLdsMax / lds);
-  const int per_cu = by_lds < res.wg_per_cu ? (by_lds > 0 ? by_lds : 1) : res.wg_per_cu;
+  int per_cu = by_lds < res.wg_per_cu ? (by_lds > 0 ? by_lds : 1) : res.wg_per_cu;
+  if (per_cu > max_per_cu) per_cu = max_per_cu;
   const uint32_t resident = (uint32_t)(per_cu * res.cus);
   const uint32_t grid = ntiles < resident ? ntiles : resident;
   hipLaunchKernelGGL(KERN, dim3(grid), dim3(threads), lds, stream, a, b, c, N, K, M);
@@ -693,6 +695,14 @@ hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32
   const auto *b = static_cast<const uint8_t *>(B);
   auto *c = static_cast<uint16_t *>(C);
   constexpr int NW = 8;
+  // Measured on MI355X (graph-replayed, cold weights, N = K = 5120 unless
+  // stated): two block pairs in flight per wave at one row, three for
+  // batched rows (M = 2: 6.02 -> 5.51 us, M = 4: 7.63 -> 6.90, N = 17408
+  // M = 8: 13.8 -> 12.5; at M = 1 three cost 5.28 -> 5.54); and at most two
+  // workgroups per compute unit up to two rows (M = 1: 5.28 -> 4.88 us,
+  // N = 5120 K = 17408: 12.1 -> 10.6), one beyond (M = 4: 6.96 -> 6.65).
+  constexpr int kDepth = MMAX == 1 ? 2 : 3;
+  constexpr int kMaxPerCu = MMAX <= 2 ? 2 : 1;
   const size_t lds = pair_lds_bytes<MMAX>(M, K);
   const bool bounded = (uint64_t)N * (K >> 7) * kBlockBytes < (1ull << 32);  // buffer-load range
   if (lds <= kLdsMax && bounded) {  // activations fit in LDS: the pairs kernel
@@ -706,17 +716,17 @@ hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32
     if (!wfirst) {
       if constexpr (MMAX == 1) {
         if (per_thread <= 2)
-          return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 2, false>>(64 * NW, lds, ntiles, stream, a, b, c, N, K, M);
+          return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 2, false>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
         if (per_thread <= 4)
-          return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 4, false>>(64 * NW, lds, ntiles, stream, a, b, c, N, K, M);
-        return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 10, false>>(64 * NW, lds, ntiles, stream, a, b, c, N, K, M);
+          return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 4, false>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
+        return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 10, false>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
       }
     }
     if (per_thread <= 2)
-      return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 2, true>>(64 * NW, lds, ntiles, stream, a, b, c, N, K, M);
+      return launch_persistent<q2_0_pairs_kernel<MMAX, NW, kDepth, 2, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
     if (per_thread <= 4)
-      return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 4, true>>(64 * NW, lds, ntiles, stream, a, b, c, N, K, M);
-    return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 10, true>>(64 * NW, lds, ntiles, stream, a, b, c, N, K, M);
+      return launch_persistent<q2_0_pairs_kernel<MMAX, NW, kDepth, 4, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
+    return launch_persistent<q2_0_pairs_kernel<MMAX, NW, kDepth, 10, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
   }
   // else per phase (same bits)
   return launch_phase<MMAX>(a, b, c, N, K, M, stream);
