@@ -375,19 +375,23 @@ __global__ __launch_bounds__(kThreads) void w8a16_units_kernel(const uint16_t *_
   {  // A into LDS while the first DEPTH blocks are in flight
     const uint32_t cpr = K >> 3;
     const uint32_t total = M * cpr;
-    const uint32_t spare = tid % total;
     u32x4_t av[UA];
     uint32_t adst[UA];
+    // chunk c: row m = c / cpr, counted with MMAX - 1 compares (no division);
+    // idle slots re-read chunk 0 and write into the partials
     auto a_load = [&](uint32_t base) {
 #pragma unroll
       for (int u = 0; u < UA; ++u) {
         const uint32_t c = base + (uint32_t)u * kThreads + tid;
         const bool in = c < total;
-        const uint32_t cc = in ? c : spare;
-        const uint32_t m = cc / cpr, col = cc - m * cpr;
+        const uint32_t cc = in ? c : 0u;
+        uint32_t m = 0;
+#pragma unroll
+        for (int x = 1; x < MMAX; ++x) m += cc >= (uint32_t)x * cpr ? 1u : 0u;
+        const uint32_t col = cc - m * cpr;
         av[u] = *reinterpret_cast<const u32x4_t *>(reinterpret_cast<const uint8_t *>(A) + (size_t)m * lda * 2u +
                                                    16u * col);
-        adst[u] = in ? L::kA + m * a_pitch + 16u * col : (uint32_t)L::kPart;  // idle: into the partials
+        adst[u] = in ? L::kA + m * a_pitch + 16u * col : (uint32_t)L::kPart;
       }
     };
     auto a_store = [&]() {

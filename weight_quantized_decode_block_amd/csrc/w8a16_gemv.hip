@@ -159,7 +159,10 @@ __global__ __launch_bounds__(kThreads) void w8a16_gemv_kernel(const uint16_t *__
      // zeros past K
     const uint32_t total = M * nchunk * 128u;
     auto piece = [&](uint32_t x, u32x4_t &v, uint32_t &dst) __attribute__((always_inline)) {
-      const uint32_t m = x / (nchunk * 128u), rest = x - m * (nchunk * 128u);
+      uint32_t m = 0;  // x / (nchunk * 128) with MMAX - 1 compares (no division)
+#pragma unroll
+      for (int j = 1; j < MMAX; ++j) m += x >= (uint32_t)j * nchunk * 128u ? 1u : 0u;
+      const uint32_t rest = x - m * (nchunk * 128u);
       const uint32_t c = rest >> 7, p = rest & 127u;
       const uint32_t k = 1024u * c + 8u * p;
       const u32x4_t zero = {0u, 0u, 0u, 0u};
