@@ -95,6 +95,32 @@ def test_ffn_shapes(oracle_mod, N, K):
     check_parity(got32[16:, cols], ref, f"w8a16 {N}x{K} rows 16..31 sampled")
 
 
+@pytest.mark.parametrize("N,K,M", [(5120, 17408, 5), (5120, 17408, 8), (5120, 17408, 12), (1000, 16512, 9),
+                                   (17408, 9216, 10), (300, 17408, 7)])
+def test_activations_larger_than_lds(oracle_mod, N, K, M):
+    """Activations larger than LDS (M x K x 2 bytes over 160 KB) are staged in
+    segments of K: every row equals its own M=1 call (which keeps all of A in
+    LDS) bit for bit, the 64-row-band call gives the same bits, and sampled
+    columns are within the parity bar.  Covers K not a multiple of 1024
+    (16512), a workgroup with five 16-row tiles (N = 17408) and one tile
+    (N = 300)."""
+    from weight_quantized_decode_block_amd import wqd
+    A, W, S = _case(31, N, K, M, salt=N + K)
+    Wd, Sd = dev_u8(W), dev_f32(S)
+    got = w8a16_gpu(A, Wd, Sd, N, K)
+    for m in range(M):
+        assert np.array_equal(w8a16_gpu(A[m:m + 1], Wd, Sd, N, K), got[m:m + 1]), f"row {m}"
+    C = torch.full((16, N), CANARY, dtype=torch.int16, device="cuda")
+    wqd.w8a16_gemm_m16_n64(dev_u16(A), Wd, Sd, C, M, N, K)
+    torch.cuda.synchronize()
+    band = host_u16(C)
+    assert np.array_equal(band[:M], got)
+    assert np.all(band[M:] == CANARY)
+    cols = np.sort(gen.rng(907, N, K).choice(N, min(N, 256), replace=False))
+    ref = np.concatenate([oracle_mod.w8a16_gemm(A, W[c:c + 1], S[c // 128:c // 128 + 1]) for c in cols], axis=1)
+    check_parity(got[:, cols], ref, f"w8a16 {N}x{K} M={M} sampled")
+
+
 # --------------------------------------------- _n64 and _strided variants
 def _contiguous(A, Wd, Sd, N, K):
     return w8a16_gpu(A, Wd, Sd, N, K)

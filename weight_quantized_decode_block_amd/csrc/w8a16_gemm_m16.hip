@@ -636,6 +636,247 @@ hipError_t launch_regs(const void *A, const void *W, const float *S, void *C, ui
                                               static_cast<uint16_t *>(C), M, N, K, lda, ldc);
 }
 
+// ---------------------------------------------------------------------------
+// Segmented kernel (activations too large for LDS): the same tiles, block
+// ownership, arithmetic and reduction order as the kernels above, so the same
+// bits.
+//   * One workgroup per CU owns rows [r0, r1) (an even split of N, or 16 * band
+//     rows) as T <= TMAX tiles of 16 rows.  K is walked in segments of SB
+//     blocks; the activation rows of a segment are staged in LDS once per
+//     workgroup (two buffers: the next segment's loads are in flight while the
+//     current one is used, one barrier per segment) and serve all T tiles.
+//   * Wave w owns blocks w, w + 8, ... (SB is a multiple of 8, so a wave meets
+//     its blocks in ascending order).  A unit is one such block for all T
+//     tiles: the lane's 64 activation bytes are read from LDS once and feed T
+//     chains of four MFMA, one per tile, and each tile keeps its own outer
+//     accumulator (outer_t = outer_t + s * inner).
+//   * Weights go straight from memory to the lanes as in the units kernel,
+//     DEPTH units ahead, across segment boundaries.
+//   * After the last segment the 8 waves' partial tiles are added in LDS in
+//     wave order and rows m < M are stored.
+// ---------------------------------------------------------------------------
+template <int MMAX, int TMAX>
+struct SegRegs {
+  u32x4_t w0[TMAX], w1[TMAX];  // this lane's 32 FP8 weights of the block, per tile
+  float s[TMAX];               // the block's scale for this lane's row, per tile
+};
+
+template <int MMAX>
+struct SegShape {
+  static constexpr int kSB = MMAX <= 8 ? 32 : 16;             // blocks per segment
+  static constexpr int kPitch = kSB * 256 + 16;               // LDS pitch of an activation row segment
+  static constexpr int kBuf = MMAX * kPitch;                  // one segment buffer
+  static constexpr int kChunks = MMAX * kSB * 16 / kThreads;  // 16-byte chunks per thread per segment
+  static_assert(kSB % kWaves == 0, "a wave must meet its blocks in ascending order");
+  static_assert(MMAX * kSB * 16 % kThreads == 0, "whole staging rounds");
+};
+
+template <int MMAX, int TMAX, int DEPTH>
+__global__ __launch_bounds__(kThreads) void w8a16_segs_kernel(const uint16_t *__restrict__ A,
+                                                              const uint8_t *__restrict__ W,
+                                                              const float *__restrict__ S,
+                                                              uint16_t *__restrict__ C, uint32_t M, uint32_t N,
+                                                              uint32_t K, uint32_t lda, uint32_t ldc,
+                                                              uint32_t band) {
+  using G = SegShape<MMAX>;
+  constexpr int NF = MMAX < 4 ? MMAX : 4;
+  constexpr uint32_t kSB = G::kSB, kUps = kSB / kWaves;  // units per wave per full segment
+  static_assert(kUps % DEPTH == 0, "a segment's units fill whole rounds of the ring");
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const uint32_t tid = threadIdx.x;
+  const uint32_t lane = tid & 63u;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t i = lane & 15u, g = lane >> 4;
+  const uint32_t nb = K >> 7;
+  uint32_t r0, r1;
+  if (band == 0u) {
+    r0 = (uint32_t)(((uint64_t)N * blockIdx.x) / gridDim.x);
+    r1 = (uint32_t)(((uint64_t)N * (blockIdx.x + 1u)) / gridDim.x);
+  } else {
+    r0 = blockIdx.x * 16u * band;
+    r1 = min(r0 + 16u * band, N);
+  }
+  const uint32_t T = (r1 - r0 + 15u) >> 4;  // <= TMAX (checked by the launcher)
+  const uint32_t nseg = (nb + kSB - 1u) / kSB;
+  const uint32_t nq = nb > wave ? (nb - wave + kWaves - 1) / kWaves : 0u;  // the wave's blocks
+
+  const __amdgpu_buffer_rsrc_t wrsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(W), (short)0, (int)(N * K), 0x00020000);
+  const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float *>(S), (short)0, (int)(((N + 127u) >> 7) * nb * 4u), 0x00020000);
+
+  // unit q of this wave is block wave + 8q for every tile
+  uint32_t lq = 0;  // next unit to request
+  const uint32_t w_lane = 32u * g;
+  auto issue_next = [&]() {
+    const bool live = lq < nq;
+    const uint32_t b = live ? wave + kWaves * lq : 0u;
+    SegRegs<MMAX, TMAX> r;
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      const uint32_t row = r0 + 16u * (uint32_t)t + i;
+      const bool in = live && (uint32_t)t < T && row < r1;
+      const uint32_t voff = in ? row * K + w_lane : kPastEnd;
+      r.w0[t] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, voff, 128u * b, 0);
+      r.w1[t] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, voff + 16u, 128u * b, 0);
+      const uint32_t srow = (row < r1 ? row : r1 - 1u) >> 7;
+      r.s[t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                             srsrc, in ? srow * nb * 4u : kPastEnd, 4u * b, 0));
+    }
+    ++lq;
+    return r;
+  };
+
+  // staging: chunk c = u * 512 + tid of segment sg is activation row c / (16 SB),
+  // 16-byte column c % (16 SB); rows >= M and columns past K are not staged
+  u32x4_t av[G::kChunks];
+  auto stage_load = [&](uint32_t sg) {
+#pragma unroll
+    for (int u = 0; u < G::kChunks; ++u) {
+      const uint32_t c = (uint32_t)u * kThreads + tid;
+      const uint32_t m = c / (kSB * 16u), col = c % (kSB * 16u);
+      const uint32_t k = sg * kSB * 128u + 8u * col;
+      const bool ok = m < M && k < K;
+      av[u] = *reinterpret_cast<const u32x4_t *>(A + (ok ? (size_t)m * lda + k : 0u));
+    }
+  };
+  auto stage_store = [&](uint32_t sg) {
+    uint8_t *buf = lds + (sg & 1u) * G::kBuf;
+#pragma unroll
+    for (int u = 0; u < G::kChunks; ++u) {
+      const uint32_t c = (uint32_t)u * kThreads + tid;
+      const uint32_t m = c / (kSB * 16u), col = c % (kSB * 16u);
+      const uint32_t k = sg * kSB * 128u + 8u * col;
+      if (m < M && k < K) *reinterpret_cast<u32x4_t *>(buf + m * G::kPitch + 16u * col) = av[u];
+    }
+  };
+
+  SegRegs<MMAX, TMAX> ring[DEPTH];
+  stage_load(0u);
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) ring[d] = issue_next();
+  stage_store(0u);
+  __syncthreads();
+  if (nseg > 1u) stage_load(1u);
+
+  f32x4_t outer[TMAX];
+#pragma unroll
+  for (int t = 0; t < TMAX; ++t) outer[t] = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
+  const uint32_t a_lane = (i < M ? i : 0u) * G::kPitch + 64u * g;  // rows >= M read row 0, never stored
+  auto unit = [&](const SegRegs<MMAX, TMAX> &r, uint32_t b, uint32_t sg) {
+    const uint8_t *act = lds + (sg & 1u) * G::kBuf + a_lane + 256u * (b - sg * kSB);
+    bf16x8_t a[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = *reinterpret_cast<const bf16x8_t *>(act + 16 * j);
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      if ((uint32_t)t < T) {
+        f32x4_t x = {0.0f, 0.0f, 0.0f, 0.0f};
+        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], weights8(r.w0[t].x, r.w0[t].y), x, 0, 0, 0);
+        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], weights8(r.w0[t].z, r.w0[t].w), x, 0, 0, 0);
+        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2], weights8(r.w1[t].x, r.w1[t].y), x, 0, 0, 0);
+        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[3], weights8(r.w1[t].z, r.w1[t].w), x, 0, 0, 0);
+#pragma unroll
+        for (int rr = 0; rr < NF; ++rr) outer[t][rr] = __fadd_rn(outer[t][rr], __fmul_rn(r.s[t], x[rr]));
+      }
+    }
+  };
+
+  uint32_t q = 0;  // next unit to compute
+  for (uint32_t sg = 0; sg < nseg; ++sg) {
+    for (uint32_t u0 = 0; u0 < kUps; u0 += DEPTH) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+        if (q < nq && q < (sg + 1u) * kUps) {
+          unit(ring[d], wave + kWaves * q, sg);
+          ring[d] = issue_next();
+          ++q;
+        }
+      }
+    }
+    if (sg + 1u < nseg) {
+      stage_store(sg + 1u);  // that buffer was last read in segment sg - 1, before the previous barrier
+      __syncthreads();
+      if (sg + 2u < nseg) stage_load(sg + 2u);
+    }
+  }
+
+  // the 8 waves' partial tiles, added in wave order
+  __syncthreads();  // every wave is done with the segment buffers
+  float *part = reinterpret_cast<float *>(lds);  // [tile][wave][m][16]
+#pragma unroll
+  for (int t = 0; t < TMAX; ++t) {
+    if ((uint32_t)t < T) {
+#pragma unroll
+      for (int rr = 0; rr < NF; ++rr) {
+        const uint32_t m = 4u * g + rr;
+        if (m < M) part[(((uint32_t)t * kWaves + wave) * MMAX + m) * 16u + i] = outer[t][rr];
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < M * 16u) {
+    const uint32_t m = tid >> 4, col = tid & 15u;
+    for (uint32_t t = 0; t < T; ++t) {
+      const uint32_t n = r0 + 16u * t + col;
+      if (n < r1) {
+        const float *pp = part + (t * kWaves * MMAX + m) * 16u + col;
+        float v = pp[0];
+        for (uint32_t w = 1; w < kWaves; ++w) v = v + pp[w * MMAX * 16u];
+        C[(size_t)m * ldc + n] = f32_to_bf16_rne(v);
+      }
+    }
+  }
+}
+
+template <int MMAX, int TMAX>
+hipError_t launch_segs_t(uint32_t grid, hipStream_t stream, const void *A, const void *W, const float *S, void *C,
+                         uint32_t M, uint32_t N, uint32_t K, uint32_t lda, uint32_t ldc, uint32_t band) {
+  constexpr auto kern = w8a16_segs_kernel<MMAX, TMAX, 2>;
+  constexpr size_t lds = 2u * SegShape<MMAX>::kBuf;
+  static_assert(lds <= 160u * 1024u, "two segment buffers must fit in LDS");
+  static_assert((size_t)TMAX * kWaves * MMAX * 16u * 4u <= lds, "the partial tiles reuse the segment buffers");
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, stream, static_cast<const uint16_t *>(A),
+                     static_cast<const uint8_t *>(W), S, static_cast<uint16_t *>(C), M, N, K, lda, ldc, band);
+  return hipGetLastError();
+}
+
+// Tiles per workgroup of the segmented kernel's grid: one workgroup per CU
+// (an even row split) or one per band of 16 * band rows.
+struct SegGrid {
+  uint32_t grid, tiles;
+};
+inline hipError_t seg_grid(uint32_t N, uint32_t band, SegGrid &sg) {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    cus = n > 0 ? n : 1;
+  }
+  const uint32_t ntiles = (N + 15u) / 16u;
+  if (band > 0u) {
+    sg.grid = (ntiles + band - 1u) / band;
+    sg.tiles = band;
+  } else {
+    sg.grid = ntiles < (uint32_t)cus ? ntiles : (uint32_t)cus;
+    sg.tiles = ((N + sg.grid - 1u) / sg.grid + 15u) / 16u;
+  }
+  return hipSuccess;
+}
+
+template <int MMAX>
+hipError_t launch_segs(const SegGrid &sg, hipStream_t stream, const void *A, const void *W, const float *S, void *C,
+                       uint32_t M, uint32_t N, uint32_t K, uint32_t lda, uint32_t ldc, uint32_t band) {
+  if (sg.tiles <= 2u) return launch_segs_t<MMAX, 2>(sg.grid, stream, A, W, S, C, M, N, K, lda, ldc, band);
+  if (sg.tiles <= 3u) return launch_segs_t<MMAX, 3>(sg.grid, stream, A, W, S, C, M, N, K, lda, ldc, band);
+  return launch_segs_t<MMAX, 5>(sg.grid, stream, A, W, S, C, M, N, K, lda, ldc, band);
+}
+
 }  // namespace
 
 hipError_t launch_w8a16_m16(const void *A, const void *W, const float *S, void *C, uint32_t M, uint32_t N,
@@ -658,6 +899,17 @@ hipError_t launch_w8a16_m16(const void *A, const void *W, const float *S, void *
     if (M <= 2) return launch_units_mmax<2>(A, W, S, C, M, N, K, lda, ldc, band, stream);
     if (M <= 4) return launch_units_mmax<4>(A, W, S, C, M, N, K, lda, ldc, band, stream);
     return launch_units_mmax<8>(A, W, S, C, M, N, K, lda, ldc, band, stream);
+  }
+  // activations larger than LDS: segments of K staged once per workgroup for
+  // all its tiles, up to 5 tiles (80 rows) per workgroup
+  if (bounded) {
+    SegGrid sg;
+    const hipError_t e = seg_grid(N, band, sg);
+    if (e != hipSuccess) return e;
+    if (sg.tiles <= 5u) {
+      if (M <= 8) return launch_segs<8>(sg, stream, A, W, S, C, M, N, K, lda, ldc, band);
+      return launch_segs<16>(sg, stream, A, W, S, C, M, N, K, lda, ldc, band);
+    }
   }
   if (M <= 4) return launch_slots<slots_for(4)>(A, W, S, C, M, N, K, lda, ldc, band, stream);
   if (M <= 8) return launch_slots<slots_for(8)>(A, W, S, C, M, N, K, lda, ldc, band, stream);
