@@ -174,6 +174,27 @@ class Fp8ValuWorkload(Fp8Workload):
         self.dispatches = sum((min(16, M - r0) + rows - 1) // rows for r0 in range(0, M, 16))
 
 
+class ReadProbe:
+    """The workload's weight ring read by a plain coalesced kernel (no
+    arithmetic, no stores): the single-launch HBM read ceiling for the same
+    bytes, cold-cycled the same way, timed like the workload."""
+
+    def __init__(self, torch, lib, wl):
+        import ctypes
+        self.torch, self.lib, self.ring, self.R = torch, lib, wl.ring, wl.R
+        self.nbytes = (wl.ring[0].numel() * wl.ring[0].element_size()) // 16 * 16
+        self.sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        lib.wqd_bench_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+        lib.wqd_bench_read.restype = ctypes.c_int
+
+    def call(self, wqd, i):
+        t = self.ring[i % self.R]
+        rc = self.lib.wqd_bench_read(t.data_ptr(), self.nbytes, self.sink.data_ptr(),
+                                     self.torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"wqd_bench_read failed with hipError {rc}")
+
+
 HEADLINE = ("q2_0 M=1 N=5120 K=5120", Q2Workload, 2, 5120, 5120, 1)
 
 
@@ -285,6 +306,12 @@ def main():
     torch.cuda.set_device(0)
     wqd.lib()
 
+    import ctypes
+    from weight_quantized_decode_block_amd import build as hip_build
+    if not os.path.exists(hip_build.BENCH_LIB):
+        sys.exit(f"{hip_build.BENCH_LIB} is missing: build first (python -m weight_quantized_decode_block_amd.build)")
+    read_lib = ctypes.CDLL(hip_build.BENCH_LIB)
+
     import oracle  # parity checks and the CPU baseline only
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from parity import check_parity
@@ -299,14 +326,20 @@ def main():
         wl.check(torch, np, oracle, lambda g, r: check_parity(g, r, name), 0)
         wl.check(torch, np, oracle, lambda g, r: check_parity(g, r, name), wl.R // 2 + 1)
         step_ms, eager_ms = time_workload(torch, wqd, wl, steps, warmup)
+        probe = ReadProbe(torch, read_lib, wl)
+        read_ms, _ = time_workload(torch, wqd, probe, steps, warmup)
         res = {"workload": name, "format": wl.fmt, "N": N, "K": K, "M": M, "ring": wl.R,
                "dispatches": wl.dispatches, "bytes_per_call": wl.bytes,
                "us_per_call": round(step_ms * 1e3, 3),
                "gbs": round(wl.bytes / (step_ms * 1e-3) / 1e9, 1),
-               "us_per_call_eager": round(eager_ms * 1e3, 3)}
+               "us_per_call_eager": round(eager_ms * 1e3, 3),
+               "read_ceiling_us": round(read_ms * 1e3, 3),
+               "read_ceiling_gbs": round(probe.nbytes / (read_ms * 1e-3) / 1e9, 1)}
         res["frac_hbm"] = round(res["gbs"] / HBM_PEAK_GBS, 4)
+        res["frac_read_ceiling"] = round(read_ms / step_ms, 4)
         log(f"[bench] {name}: {res['us_per_call']} us/call, {res['gbs']} GB/s, "
-            f"{100 * res['frac_hbm']:.1f}% of HBM peak (eager launches: {res['us_per_call_eager']} us/call)")
+            f"{100 * res['frac_hbm']:.1f}% of HBM peak (eager launches: {res['us_per_call_eager']} us/call); "
+            f"plain read of the same ring {res['read_ceiling_us']} us ({res['read_ceiling_gbs']} GB/s)")
         return wl, res
 
     if args.copy_probe:
@@ -383,6 +416,10 @@ def main():
                      "traffic": traffic_from_profile(kern_src, "q2_0_gemv_kernel_m1_5120x5120"),
                      "kernel": "q2_0_pairs_kernel<1, 8, 2, 2, false>", "kernel_us_avg": head["us_per_call"]},
         "cpu_baseline": cpu,
+        "read_ceiling": {"us_per_call": head["read_ceiling_us"], "gbs": head["read_ceiling_gbs"],
+                         "frac": head["frac_read_ceiling"],
+                         "kernel": "plain coalesced read of the same weight ring copies, graph-replayed "
+                                   "(libwqd_bench.so); frac = its time / the GEMV's time"},
     }
     if sweep:
         line["sweep"] = sweep

@@ -12,6 +12,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libwqd.so")
+# bench-only helper (a plain read of a buffer: the read ceiling bench.py reports)
+BENCH_LIB = os.path.join(PKG, "libwqd_bench.so")
 SOURCES = ["api.cpp", "pack.cpp", "q2_0_mfma.hip", "q2_0_valu.hip", "w8a16_gemm_m16.hip", "w8a16_gemv.hip"]
 ARCH = "gfx950"
 
@@ -41,6 +43,12 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    tmp = BENCH_LIB + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, "-x", "hip", os.path.join(CSRC, "bench_read.hip"), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, BENCH_LIB)
     return LIB
 
 
