@@ -221,8 +221,8 @@ __global__ __launch_bounds__(kThreads) void q2_0_phase_kernel(const uint16_t *__
   const uint32_t nphase = (nb + kPhaseBlocks - 1) / kPhaseBlocks;
   const uint32_t tail_blocks = nb - (nphase - 1u) * kPhaseBlocks;  // 8 or 16
   const size_t rb = (size_t)nb * kBlockBytes;
-  const uint32_t r0 = (uint32_t)(((uint64_t)N * blockIdx.x) / gridDim.x);
-  const uint32_t r1 = (uint32_t)(((uint64_t)N * (blockIdx.x + 1u)) / gridDim.x);
+  uint32_t r0, r1;
+  even_rows(N, blockIdx.x, gridDim.x, r0, r1);
   // This workgroup's super-tiles start at r0, r0 + kSpan, ...; its phases
   // form one sequence over them, and the load ring runs across super-tile
   // boundaries so the next one's first phases are in flight when one ends.

@@ -320,8 +320,7 @@ __global__ __launch_bounds__(kThreads) void w8a16_units_kernel(const uint16_t *_
   // 16 * band rows from blockIdx.x * 16 * band
   uint32_t r0, r1;
   if (band == 0u) {
-    r0 = (uint32_t)(((uint64_t)N * blockIdx.x) / gridDim.x);
-    r1 = (uint32_t)(((uint64_t)N * (blockIdx.x + 1u)) / gridDim.x);
+    even_rows(N, blockIdx.x, gridDim.x, r0, r1);
   } else {
     r0 = blockIdx.x * 16u * band;
     r1 = min(r0 + 16u * band, N);
@@ -545,8 +544,7 @@ __global__ __launch_bounds__(kThreads) void w8a16_regs_kernel(const uint16_t *__
   const uint32_t nb = K >> 7;
   uint32_t r0, r1;  // rows of this workgroup, as in the kernel above
   if (band == 0u) {
-    r0 = (uint32_t)(((uint64_t)N * blockIdx.x) / gridDim.x);
-    r1 = (uint32_t)(((uint64_t)N * (blockIdx.x + 1u)) / gridDim.x);
+    even_rows(N, blockIdx.x, gridDim.x, r0, r1);
   } else {
     r0 = blockIdx.x * 16u * band;
     r1 = min(r0 + 16u * band, N);
@@ -690,8 +688,7 @@ __global__ __launch_bounds__(kThreads) void w8a16_segs_kernel(const uint16_t *__
   const uint32_t nb = K >> 7;
   uint32_t r0, r1;
   if (band == 0u) {
-    r0 = (uint32_t)(((uint64_t)N * blockIdx.x) / gridDim.x);
-    r1 = (uint32_t)(((uint64_t)N * (blockIdx.x + 1u)) / gridDim.x);
+    even_rows(N, blockIdx.x, gridDim.x, r0, r1);
   } else {
     r0 = blockIdx.x * 16u * band;
     r1 = min(r0 + 16u * band, N);

@@ -112,8 +112,8 @@ __global__ __launch_bounds__(kThreads) void w8a16_gemv_kernel(const uint16_t *__
   const uint32_t nb = K >> 7;
   const uint32_t nchunk = (K + 1023u) >> 10;
   const uint32_t a_pitch = nchunk * kChunkBytes;
-  const uint32_t r0 = (uint32_t)(((uint64_t)N * blockIdx.x) / gridDim.x);
-  const uint32_t r1 = (uint32_t)(((uint64_t)N * (blockIdx.x + 1u)) / gridDim.x);
+  uint32_t r0, r1;
+  even_rows(N, blockIdx.x, gridDim.x, r0, r1);
   // rows of this wave: r0 + wave + 8t for t < nrows, in groups of RPW
   const uint32_t nrows = r1 - r0 > wave ? (r1 - r0 - wave + kWaves - 1u) / kWaves : 0u;
   const uint32_t ngroups = (nrows + RPW - 1u) / RPW;

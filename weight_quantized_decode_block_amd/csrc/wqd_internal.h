@@ -6,6 +6,17 @@
 
 namespace wqd {
 
+// Rows [r0, r1) of workgroup b when N rows are split evenly over G
+// workgroups: the first N % G get one row more.  Wave-uniform 32-bit
+// arithmetic (a 64-bit division here cost about 100 instructions per wave
+// before the first load).
+__device__ __forceinline__ void even_rows(uint32_t N, uint32_t b, uint32_t G, uint32_t &r0, uint32_t &r1) {
+  const uint32_t q = N / G, rem = N - q * G;
+  r0 = b * q + (b < rem ? b : rem);
+  r1 = r0 + q + (b < rem ? 1u : 0u);
+}
+
+
 // Enqueue one batched Q2_0 launch for 1..8 rows (A [m][K], C [m][N]) on the
 // vector-ALU kernel.  Shapes are validated by the caller.
 hipError_t launch_q2_0_valu(const void *A, const void *B, void *C, uint32_t N,
