@@ -316,6 +316,33 @@ __global__ __launch_bounds__(kThreads) void w8a16_units_kernel(const uint16_t *_
   const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t i = lane & 15u, g = lane >> 4;
   const uint32_t nb = K >> 7;
+  const uint32_t a_pitch = 2u * K + 16u;
+
+  // A into LDS while the first DEPTH blocks are in flight; its first round is
+  // requested before any other set-up.  Chunk c: row m = c / cpr, counted
+  // with MMAX - 1 compares (no division); idle slots re-read chunk 0 and
+  // write into the partials.
+  const uint32_t cpr = K >> 3;
+  const uint32_t total = M * cpr;
+  u32x4_t av[UA];
+  uint32_t adst[UA];
+  auto a_load = [&](uint32_t base) {
+#pragma unroll
+    for (int u = 0; u < UA; ++u) {
+      const uint32_t c = base + (uint32_t)u * kThreads + tid;
+      const bool in = c < total;
+      const uint32_t cc = in ? c : 0u;
+      uint32_t m = 0;
+#pragma unroll
+      for (int x = 1; x < MMAX; ++x) m += cc >= (uint32_t)x * cpr ? 1u : 0u;
+      const uint32_t col = cc - m * cpr;
+      av[u] = *reinterpret_cast<const u32x4_t *>(reinterpret_cast<const uint8_t *>(A) + (size_t)m * lda * 2u +
+                                                 16u * col);
+      adst[u] = in ? L::kA + m * a_pitch + 16u * col : (uint32_t)L::kPart;
+    }
+  };
+  a_load(0u);
+
   // rows [r0, r1) of this workgroup: an even split over the grid (band = 0) or
   // 16 * band rows from blockIdx.x * 16 * band
   uint32_t r0, r1;
@@ -330,7 +357,6 @@ __global__ __launch_bounds__(kThreads) void w8a16_units_kernel(const uint16_t *_
   // owns none (K < 1024) runs one empty unit per tile to meet the barrier
   const uint32_t upw = nb > wave ? (nb - wave + kWaves - 1) / kWaves : 1u;
   const uint32_t nq = my_tiles * upw;
-  const uint32_t a_pitch = 2u * K + 16u;
 
   const __amdgpu_buffer_rsrc_t wrsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(W), (short)0, (int)(N * K), 0x00020000);
@@ -371,33 +397,11 @@ __global__ __launch_bounds__(kThreads) void w8a16_units_kernel(const uint16_t *_
   float *part = reinterpret_cast<float *>(lds + L::kPart);
 
   UnitRegs ring[DEPTH];
-  {  // A into LDS while the first DEPTH blocks are in flight
-    const uint32_t cpr = K >> 3;
-    const uint32_t total = M * cpr;
-    u32x4_t av[UA];
-    uint32_t adst[UA];
-    // chunk c: row m = c / cpr, counted with MMAX - 1 compares (no division);
-    // idle slots re-read chunk 0 and write into the partials
-    auto a_load = [&](uint32_t base) {
-#pragma unroll
-      for (int u = 0; u < UA; ++u) {
-        const uint32_t c = base + (uint32_t)u * kThreads + tid;
-        const bool in = c < total;
-        const uint32_t cc = in ? c : 0u;
-        uint32_t m = 0;
-#pragma unroll
-        for (int x = 1; x < MMAX; ++x) m += cc >= (uint32_t)x * cpr ? 1u : 0u;
-        const uint32_t col = cc - m * cpr;
-        av[u] = *reinterpret_cast<const u32x4_t *>(reinterpret_cast<const uint8_t *>(A) + (size_t)m * lda * 2u +
-                                                   16u * col);
-        adst[u] = in ? L::kA + m * a_pitch + 16u * col : (uint32_t)L::kPart;
-      }
-    };
+  {
     auto a_store = [&]() {
 #pragma unroll
       for (int u = 0; u < UA; ++u) *reinterpret_cast<u32x4_t *>(lds + adst[u]) = av[u];
     };
-    a_load(0u);
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) ring[d] = issue_next();
     a_store();

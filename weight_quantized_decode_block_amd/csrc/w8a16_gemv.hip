@@ -112,6 +112,42 @@ __global__ __launch_bounds__(kThreads) void w8a16_gemv_kernel(const uint16_t *__
   const uint32_t nb = K >> 7;
   const uint32_t nchunk = (K + 1023u) >> 10;
   const uint32_t a_pitch = nchunk * kChunkBytes;
+
+  // Activations into LDS: 16-byte piece p of chunk c of row m holds
+  // A[m][1024c + 8p .. +7] at m * a_pitch + 2048c + 1024(p & 1) + 16(p >> 1),
+  // zeros past K.  The first round of loads is requested before any other
+  // set-up (the waves of a CU issue their scalar set-up one at a time).
+  const uint32_t total = M * nchunk * 128u;
+  auto piece = [&](uint32_t x, u32x4_t &v, uint32_t &dst) __attribute__((always_inline)) {
+    uint32_t m = 0;  // x / (nchunk * 128) with MMAX - 1 compares (no division)
+#pragma unroll
+    for (int j = 1; j < MMAX; ++j) m += x >= (uint32_t)j * nchunk * 128u ? 1u : 0u;
+    const uint32_t rest = x - m * (nchunk * 128u);
+    const uint32_t c = rest >> 7, p = rest & 127u;
+    const uint32_t k = 1024u * c + 8u * p;
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+    v = k < K ? *reinterpret_cast<const u32x4_t *>(A + (size_t)m * lda + k) : zero;
+    dst = m * a_pitch + kChunkBytes * c + 1024u * (p & 1u) + 16u * (p >> 1);
+  };
+  constexpr int UA = 4;
+  u32x4_t av[UA];
+  uint32_t adst[UA];
+  auto a_load = [&](uint32_t base) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < UA; ++u) {
+      const uint32_t x = base + (uint32_t)u * kThreads + tid;
+      if (x < total) piece(x, av[u], adst[u]);
+    }
+  };
+  auto a_store = [&](uint32_t base) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < UA; ++u) {
+      const uint32_t x = base + (uint32_t)u * kThreads + tid;
+      if (x < total) *reinterpret_cast<u32x4_t *>(lds + adst[u]) = av[u];
+    }
+  };
+  a_load(0u);
+
   uint32_t r0, r1;
   even_rows(N, blockIdx.x, gridDim.x, r0, r1);
   // rows of this wave: r0 + wave + 8t for t < nrows, in groups of RPW
@@ -154,35 +190,11 @@ __global__ __launch_bounds__(kThreads) void w8a16_gemv_kernel(const uint16_t *__
 
   static_assert(DEPTH % RPW == 0, "a ring position must always serve the same row slot");
   ChunkRegs ring[DEPTH];
-  {  // activations into LDS: 16-byte piece p of chunk c of row m holds
-     // A[m][1024c + 8p .. +7] at m * a_pitch + 2048c + 1024(p & 1) + 16(p >> 1),
-     // zeros past K
-    const uint32_t total = M * nchunk * 128u;
-    auto piece = [&](uint32_t x, u32x4_t &v, uint32_t &dst) __attribute__((always_inline)) {
-      uint32_t m = 0;  // x / (nchunk * 128) with MMAX - 1 compares (no division)
-#pragma unroll
-      for (int j = 1; j < MMAX; ++j) m += x >= (uint32_t)j * nchunk * 128u ? 1u : 0u;
-      const uint32_t rest = x - m * (nchunk * 128u);
-      const uint32_t c = rest >> 7, p = rest & 127u;
-      const uint32_t k = 1024u * c + 8u * p;
-      const u32x4_t zero = {0u, 0u, 0u, 0u};
-      v = k < K ? *reinterpret_cast<const u32x4_t *>(A + (size_t)m * lda + k) : zero;
-      dst = m * a_pitch + kChunkBytes * c + 1024u * (p & 1u) + 16u * (p >> 1);
-    };
-    constexpr int UA = 4;
-    for (uint32_t base = 0; base < total; base += UA * kThreads) {
-      u32x4_t v[UA];
-      uint32_t dst[UA];
-#pragma unroll
-      for (int u = 0; u < UA; ++u) {
-        const uint32_t x = base + (uint32_t)u * kThreads + tid;
-        if (x < total) piece(x, v[u], dst[u]);
-      }
-#pragma unroll
-      for (int u = 0; u < UA; ++u) {
-        const uint32_t x = base + (uint32_t)u * kThreads + tid;
-        if (x < total) *reinterpret_cast<u32x4_t *>(lds + dst[u]) = v[u];
-      }
+  {
+    a_store(0u);
+    for (uint32_t base = UA * kThreads; base < total; base += UA * kThreads) {
+      a_load(base);
+      a_store(base);
     }
     __syncthreads();
     unroll<0, DEPTH>([&](auto d) __attribute__((always_inline)) { ring[decltype(d)::value] = issue_next(); });
