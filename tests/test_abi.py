@@ -41,6 +41,21 @@ def test_product_library_does_not_link_the_oracle():
     assert b"oracle_" not in blob and b"liboracle" not in blob
 
 
+def test_bench_read_helper_is_outside_the_product_library():
+    """The plain-read kernel bench.py reports as the read ceiling lives in its
+    own library; the product C ABI neither exports nor contains it."""
+    import ctypes
+    from weight_quantized_decode_block_amd import build as hip_build
+    assert b"wqd_bench_read" not in open(wqd.LIB_PATH, "rb").read()
+    helper = ctypes.CDLL(hip_build.BENCH_LIB)
+    assert hasattr(helper, "wqd_bench_read")
+    helper.wqd_bench_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+    helper.wqd_bench_read.restype = ctypes.c_int
+    # argument checks come before any HIP call: null pointer, size not a multiple of 16
+    assert helper.wqd_bench_read(None, 16, 256, None) != 0
+    assert helper.wqd_bench_read(256, 17, 256, None) != 0
+
+
 # ------------------------------------------------------------- validation
 @pytest.mark.parametrize("args,code,frag", [
     ((None, FAKE, FAKE, 16, 1024, 128), wqd.WQD_ENULL, "non-NULL"),
