@@ -546,6 +546,17 @@ __global__ __launch_bounds__(kThreads) void w8a16_regs_kernel(const uint16_t *__
   const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t i = lane & 15u, g = lane >> 4;
   const uint32_t nb = K >> 7;
+  // the activations of the wave's blocks, requested before any other set-up
+  bf16x8_t a[NBW][4];
+  {
+    const uint16_t *arow = A + (size_t)(i < M ? i : 0u) * lda + 32u * g;
+    unroll<0, NBW>([&](auto uu) __attribute__((always_inline)) {
+      constexpr int u = decltype(uu)::value;
+      const uint32_t b = min(wave + kWaves * (uint32_t)u, nb - 1u);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[u][j] = *reinterpret_cast<const bf16x8_t *>(arow + 128u * b + 8u * j);
+    });
+  }
   uint32_t r0, r1;  // rows of this workgroup, as in the kernel above
   if (band == 0u) {
     even_rows(N, blockIdx.x, gridDim.x, r0, r1);
@@ -575,16 +586,8 @@ __global__ __launch_bounds__(kThreads) void w8a16_regs_kernel(const uint16_t *__
     return r;
   };
 
-  bf16x8_t a[NBW][4];
   UnitRegs ring[NBW];
   {
-    const uint16_t *arow = A + (size_t)(i < M ? i : 0u) * lda + 32u * g;
-    unroll<0, NBW>([&](auto uu) __attribute__((always_inline)) {
-      constexpr int u = decltype(uu)::value;
-      const uint32_t b = min(wave + kWaves * (uint32_t)u, nb - 1u);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) a[u][j] = *reinterpret_cast<const bf16x8_t *>(arow + 128u * b + 8u * j);
-    });
     unroll<0, NBW>([&](auto uu) __attribute__((always_inline)) {
       constexpr int u = decltype(uu)::value;
       ring[u] = issue(0u, (uint32_t)u);
@@ -690,6 +693,23 @@ __global__ __launch_bounds__(kThreads) void w8a16_segs_kernel(const uint16_t *__
   const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t i = lane & 15u, g = lane >> 4;
   const uint32_t nb = K >> 7;
+
+  // staging: chunk c = u * 512 + tid of segment sg is activation row c / (16 SB),
+  // 16-byte column c % (16 SB); rows >= M and columns past K are not staged.
+  // The first segment's loads go out before any other set-up.
+  u32x4_t av[G::kChunks];
+  auto stage_load = [&](uint32_t sg) {
+#pragma unroll
+    for (int u = 0; u < G::kChunks; ++u) {
+      const uint32_t c = (uint32_t)u * kThreads + tid;
+      const uint32_t m = c / (kSB * 16u), col = c % (kSB * 16u);
+      const uint32_t k = sg * kSB * 128u + 8u * col;
+      const bool ok = m < M && k < K;
+      av[u] = *reinterpret_cast<const u32x4_t *>(A + (ok ? (size_t)m * lda + k : 0u));
+    }
+  };
+  stage_load(0u);
+
   uint32_t r0, r1;
   if (band == 0u) {
     even_rows(N, blockIdx.x, gridDim.x, r0, r1);
@@ -728,19 +748,6 @@ __global__ __launch_bounds__(kThreads) void w8a16_segs_kernel(const uint16_t *__
     return r;
   };
 
-  // staging: chunk c = u * 512 + tid of segment sg is activation row c / (16 SB),
-  // 16-byte column c % (16 SB); rows >= M and columns past K are not staged
-  u32x4_t av[G::kChunks];
-  auto stage_load = [&](uint32_t sg) {
-#pragma unroll
-    for (int u = 0; u < G::kChunks; ++u) {
-      const uint32_t c = (uint32_t)u * kThreads + tid;
-      const uint32_t m = c / (kSB * 16u), col = c % (kSB * 16u);
-      const uint32_t k = sg * kSB * 128u + 8u * col;
-      const bool ok = m < M && k < K;
-      av[u] = *reinterpret_cast<const u32x4_t *>(A + (ok ? (size_t)m * lda + k : 0u));
-    }
-  };
   auto stage_store = [&](uint32_t sg) {
     uint8_t *buf = lds + (sg & 1u) * G::kBuf;
 #pragma unroll
@@ -753,7 +760,6 @@ __global__ __launch_bounds__(kThreads) void w8a16_segs_kernel(const uint16_t *__
   };
 
   SegRegs<MMAX, TMAX> ring[DEPTH];
-  stage_load(0u);
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d) ring[d] = issue_next();
   stage_store(0u);
