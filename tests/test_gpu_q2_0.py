@@ -147,12 +147,14 @@ def test_ffn_shapes(oracle_mod, N, K):
     check_parity(got32[:, cols], ref, f"q2_0 {N}x{K} M=32 sampled")
 
 
-@pytest.mark.parametrize("N,K,M", [(37, 12288, 8), (200, 12288, 7), (1, 12288, 8), (333, 17408, 6), (2049, 10240, 8)])
+@pytest.mark.parametrize("N,K,M", [(37, 12288, 8), (200, 12288, 7), (1, 12288, 8), (333, 17408, 6), (2049, 10240, 8),
+                                   (9216, 17408, 8), (10496, 17408, 5)])
 def test_large_k_batched_rows(oracle_mod, N, K, M):
     """Activations too large for LDS (the per-phase kernel with super-tiles of
-    up to four 8-row tiles over an even row split): ragged N, every row
-    bit-identical to its own M=1 launch (the resident-activation kernel) and
-    within tolerance of the oracle on a column sample."""
+    up to four 8-row tiles over an even row split; N = 9216 and 10496 on 256
+    CUs give 36 and 41 rows per workgroup, two super-tiles): ragged N, every
+    row bit-identical to its own M=1 launch (the resident-activation kernel)
+    and within tolerance of the oracle on a column sample."""
     A, codes, d, packed = _case(31, N, K, M, salt=N + K)
     Bd = dev_u8(packed)
     got = q2_0_gpu(A, Bd, N, K)
