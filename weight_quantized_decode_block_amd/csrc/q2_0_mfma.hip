@@ -516,8 +516,9 @@ __global__ __launch_bounds__(64 * NW) void q2_0_pairs_kernel(const uint16_t *__r
       for (int u = 0; u < UA; ++u) *reinterpret_cast<u32x4_t *>(lds + adst[u]) = permute_acts(av[u]);
     };
     // WFIRST: the first pairs' weights are requested before the activations
-    // (faster for large matrices and batched rows); otherwise after them
-    // (faster for one row of a small matrix, where the activation copy is on
+    // (faster for 5..8 rows, and for batched rows of large matrices);
+    // otherwise after them (the launcher's choice for one row and for 2..4
+    // rows of a small matrix, where the activation copy is on
     // the critical path)
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) ring[d] = issue_next();
@@ -703,25 +704,31 @@ hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32
   auto *c = static_cast<uint16_t *>(C);
   constexpr int NW = 8;
   // Measured on MI355X (graph-replayed, cold weights, N = K = 5120 unless
-  // stated): two block pairs in flight per wave at one row, three for
-  // batched rows (M = 2: 6.02 -> 5.51 us, M = 4: 7.63 -> 6.90, N = 17408
-  // M = 8: 13.8 -> 12.5; at M = 1 three cost 5.28 -> 5.54); and at most two
-  // workgroups per compute unit up to two rows (M = 1: 5.28 -> 4.88 us,
-  // N = 5120 K = 17408: 12.1 -> 10.6), one beyond (M = 4: 6.96 -> 6.65).
-  constexpr int kDepth = MMAX == 1 ? 2 : 3;
+  // stated): two block pairs in flight per wave with the activations
+  // requested first, three for batched rows that request the weights first
+  // (N = 17408, M = 8: 13.8 -> 12.5 us; at M = 1 three cost 5.28 -> 5.54);
+  // and at most two workgroups per compute unit up to two rows (M = 1:
+  // 5.28 -> 4.88 us, N = 5120 K = 17408: 12.1 -> 10.6), one beyond (M = 4:
+  // 6.96 -> 6.65).
+  constexpr int kDepth = 3;  // weights first
   constexpr int kMaxPerCu = MMAX <= 2 ? 2 : 1;
   const size_t lds = pair_lds_bytes<MMAX>(M, K);
   const bool bounded = (uint64_t)N * (K >> 7) * kBlockBytes < (1ull << 32);  // buffer-load range
   if (lds <= kLdsMax && bounded) {  // activations fit in LDS: the pairs kernel
     // activation chunks per thread for one staging round covering all of A
     const uint32_t per_thread = (M * (K >> 3) + 64 * NW - 1) / (64 * NW);
-    // measured on MI355X: activations first only pays for one row of a
-    // matrix under 16 MB (N = K = 5120, M = 1: 5.55 against 5.72 us; weights
-    // first: N = 17408, K = 5120, M = 1 9.7 against 10.4 us, M = 8 at
-    // N = K = 5120 6.8 against 7.0 us)
-    const bool wfirst = M > 1 || (uint64_t)N * (K >> 7) * kBlockBytes >= (16ull << 20);
+    // Activations first (their first round requested before any other
+    // set-up), or the first pairs' weights first.  Measured on MI355X
+    // (interleaved A/B, graph-replayed): activations first for one row at any
+    // size (N = 17408, K = 5120: 8.94 -> 8.48 us; N = 5120, K = 17408:
+    // 10.41 -> 9.95) and for 2..4 rows of a matrix under 16 MB (N = K = 5120,
+    // M = 2: 5.53 -> 4.86 us, M = 4: 6.68 -> 6.30); weights first for 5..8
+    // rows (even at M = 8) and for batched rows of larger matrices (N = 17408,
+    // M = 8: 12.5 against 13.7 us).
+    const bool big = (uint64_t)N * (K >> 7) * kBlockBytes >= (16ull << 20);
+    const bool wfirst = M > 4 || (M > 1 && big);
     if (!wfirst) {
-      if constexpr (MMAX == 1) {
+      if constexpr (MMAX <= 4) {
         if (per_thread <= 2)
           return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 2, false>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
         if (per_thread <= 4)
