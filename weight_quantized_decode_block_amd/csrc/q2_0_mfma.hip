@@ -707,11 +707,12 @@ hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32
   // stated): two block pairs in flight per wave with the activations
   // requested first, three for batched rows that request the weights first
   // (N = 17408, M = 8: 13.8 -> 12.5 us; at M = 1 three cost 5.28 -> 5.54);
-  // and at most two workgroups per compute unit up to two rows (M = 1:
-  // 5.28 -> 4.88 us, N = 5120 K = 17408: 12.1 -> 10.6), one beyond (M = 4:
-  // 6.96 -> 6.65).
+  // and at most two workgroups per compute unit up to four rows (M = 1:
+  // 5.28 -> 4.88 us, N = 5120 K = 17408: 12.1 -> 10.6; with the activations
+  // requested first, M = 4: 6.09 -> 5.11, N = 17408 M = 4: 12.4 -> 10.6),
+  // one beyond (eight rows of activations leave LDS for one).
   constexpr int kDepth = 3;  // weights first
-  constexpr int kMaxPerCu = MMAX <= 2 ? 2 : 1;
+  constexpr int kMaxPerCu = MMAX <= 4 ? 2 : 1;
   const size_t lds = pair_lds_bytes<MMAX>(M, K);
   const bool bounded = (uint64_t)N * (K >> 7) * kBlockBytes < (1ull << 32);  // buffer-load range
   if (lds <= kLdsMax && bounded) {  // activations fit in LDS: the pairs kernel
@@ -727,19 +728,23 @@ hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32
     // M = 8: 12.5 against 13.7 us).
     const bool big = (uint64_t)N * (K >> 7) * kBlockBytes >= (16ull << 20);
     const bool wfirst = M > 4 || (M > 1 && big);
+    // Staging chunks per thread: the smallest of 2, 3, 4, 5 and 10 that
+    // covers A in one round (idle chunk slots cost loads and registers before
+    // the staging barrier: N = K = 5120 M = 2: 4.86 -> 4.71 us, N = 5120
+    // K = 17408 M = 1: 9.92 -> 9.33).
     if (!wfirst) {
       if constexpr (MMAX <= 4) {
-        if (per_thread <= 2)
-          return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 2, false>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
-        if (per_thread <= 4)
-          return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 4, false>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
+        if (per_thread <= 2) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 2, false>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
+        if (per_thread <= 3) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 3, false>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
+        if (per_thread <= 4) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 4, false>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
+        if (per_thread <= 5) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 5, false>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
         return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 10, false>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
       }
     }
-    if (per_thread <= 2)
-      return launch_persistent<q2_0_pairs_kernel<MMAX, NW, kDepth, 2, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
-    if (per_thread <= 4)
-      return launch_persistent<q2_0_pairs_kernel<MMAX, NW, kDepth, 4, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
+    if (per_thread <= 2) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, kDepth, 2, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
+    if (per_thread <= 3) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, kDepth, 3, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
+    if (per_thread <= 4) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, kDepth, 4, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
+    if (per_thread <= 5) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, kDepth, 5, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
     return launch_persistent<q2_0_pairs_kernel<MMAX, NW, kDepth, 10, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
   }
   // else per phase (same bits)

@@ -469,7 +469,7 @@ __global__ __launch_bounds__(kThreads) void w8a16_units_kernel(const uint16_t *_
 // Launches KERN with one workgroup per 64-row band (band > 0), or with
 // kUnitWgsPerCu workgroups per CU (fewer if registers or LDS do not allow it,
 // and never fewer than 16 rows per workgroup) splitting the rows evenly.
-constexpr int kUnitWgsPerCu = 1;
+constexpr int kUnitWgsPerCu = 1;  // two measured slower on MI355X (N = K = 5120, M = 1: 7.98 -> 10.5 us)
 
 template <auto KERN>
 hipError_t launch_units(size_t lds, uint32_t ntiles, uint32_t band, hipStream_t stream, const uint16_t *a,
@@ -511,8 +511,13 @@ hipError_t launch_units_mmax(const void *A, const void *W, const float *S, void 
   const auto *w = static_cast<const uint8_t *>(W);
   auto *c = static_cast<uint16_t *>(C);
   const uint32_t per_thread = (M * (K >> 3) + kThreads - 1) / kThreads;
+  // staging chunks per thread: the smallest of 2, 3, 4, 5 and 10 covering A in
+  // one round (measured on MI355X: N = K = 5120 M = 4: 8.71 -> 8.42 us;
+  // N = 5120 K = 17408 M = 1: 20.5 -> 20.1)
   if (per_thread <= 2) return launch_units<w8a16_units_kernel<MMAX, 4, 2>>(lds, ntiles, band, stream, a, w, S, c, M, N, K, lda, ldc);
+  if (per_thread <= 3) return launch_units<w8a16_units_kernel<MMAX, 4, 3>>(lds, ntiles, band, stream, a, w, S, c, M, N, K, lda, ldc);
   if (per_thread <= 4) return launch_units<w8a16_units_kernel<MMAX, 4, 4>>(lds, ntiles, band, stream, a, w, S, c, M, N, K, lda, ldc);
+  if (per_thread <= 5) return launch_units<w8a16_units_kernel<MMAX, 4, 5>>(lds, ntiles, band, stream, a, w, S, c, M, N, K, lda, ldc);
   return launch_units<w8a16_units_kernel<MMAX, 4, 10>>(lds, ntiles, band, stream, a, w, S, c, M, N, K, lda, ldc);
 }
 
