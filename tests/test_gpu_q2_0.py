@@ -162,3 +162,25 @@ def test_large_k_batched_rows(oracle_mod, N, K, M):
         assert np.array_equal(got[m:m + 1], q2_0_gpu(A[m:m + 1], Bd, N, K, single=True)), m
     cols = np.arange(N) if N <= 400 else np.sort(gen.rng(931, N, K).choice(N, 256, replace=False))
     check_parity(got[:, cols], oracle_mod.q2_0_gemv(A, codes[cols], d[cols]), f"q2_0 {N}x{K} M={M}")
+
+
+@pytest.mark.parametrize("N,K,M", [(5120, 5120, 3), (17408, 5120, 3), (17408, 5120, 4), (5120, 17408, 2),
+                                   (5120, 17408, 3), (5120, 17408, 4), (4100, 5120, 3), (2052, 17408, 2)])
+def test_two_to_four_rows_every_staging_tier(oracle_mod, N, K, M):
+    """Two to four rows run at two workgroups per compute unit, activations
+    requested first below 16 MB of weights and weights first above, with 2, 3,
+    4, 5 or 10 staging chunks per thread (M = 3 at K = 5120 takes 4, M = 4 at
+    K = 5120 takes 5, M = 2..4 at K = 17408 take 10 over one or two rounds);
+    ragged N (4100 and 2052 end in a partial tile).  Every row bit-identical
+    to its own M=1 launch, a canary row past M untouched, a column sample
+    within tolerance of the oracle."""
+    A, codes, d, packed = _case(41, N, K, M, salt=N * 7 + K + M)
+    Bd = dev_u8(packed)
+    got = q2_0_gpu(A, Bd, N, K, extra_rows=1)
+    assert np.all(got[M] == CANARY)
+    got = got[:M]
+    for m in range(M):
+        assert np.array_equal(got[m:m + 1], q2_0_gpu(A[m:m + 1], Bd, N, K, single=True)), m
+    cols = np.sort(gen.rng(941, N, K).choice(N, 256, replace=False))
+    cols = np.union1d(cols, [N - 1])
+    check_parity(got[:, cols], oracle_mod.q2_0_gemv(A, codes[cols], d[cols]), f"q2_0 {N}x{K} M={M}")

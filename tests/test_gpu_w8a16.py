@@ -57,6 +57,25 @@ def test_rows_bit_identical_across_m(oracle_mod):
         assert np.array_equal(w8a16_gpu(A[m:m + 1], Wd, Sd, N, K), full[m:m + 1])
 
 
+@pytest.mark.parametrize("N,K,M", [(5120, 5120, 2), (5120, 5120, 3), (5120, 5120, 4), (5120, 17408, 1),
+                                   (5120, 17408, 3), (1000, 5120, 4)])
+def test_every_staging_tier_rows_bit_identical(oracle_mod, N, K, M):
+    """The resident-activation kernel's staging tiers (2, 3, 4, 5 or 10 chunks
+    per thread: M = 2, 3, 4 at K = 5120 take 3, 4, 5; M = 1 at K = 17408 takes
+    5): every row bit-identical to its own M=1 call, a column sample within
+    tolerance of the oracle."""
+    A, W, S = _case(43, N, K, M, salt=N + K + M)
+    Wd, Sd = dev_u8(W), dev_f32(S)
+    got = w8a16_gpu(A, Wd, Sd, N, K, c_rows=M + 1)
+    assert np.all(got[M] == CANARY)
+    got = got[:M]
+    for m in range(M):
+        assert np.array_equal(w8a16_gpu(A[m:m + 1], Wd, Sd, N, K), got[m:m + 1]), m
+    cols = np.sort(gen.rng(943, N, K).choice(N, 256, replace=False))
+    ref = np.concatenate([oracle_mod.w8a16_gemm(A, W[c:c + 1], S[c // 128:c // 128 + 1]) for c in cols], axis=1)
+    check_parity(got[:, cols], ref, f"w8a16 {N}x{K} M={M}")
+
+
 @pytest.mark.parametrize("N,K,M", [(130, 1024, 16), (16, 128, 1), (300, 640, 7)])
 def test_exact_integer_regime_bit_identical(oracle_mod, N, K, M):
     A = gen.exact_activations(N + M + 1, M, K)
