@@ -184,3 +184,24 @@ def test_two_to_four_rows_every_staging_tier(oracle_mod, N, K, M):
     cols = np.sort(gen.rng(941, N, K).choice(N, 256, replace=False))
     cols = np.union1d(cols, [N - 1])
     check_parity(got[:, cols], oracle_mod.q2_0_gemv(A, codes[cols], d[cols]), f"q2_0 {N}x{K} M={M}")
+
+
+@pytest.mark.parametrize("N,K,M", [(8, 5120, 8), (20, 1024, 5), (4104, 5120, 7), (17408, 5120, 6), (1032, 2048, 8),
+                                   (3, 5120, 6), (16392, 5120, 8), (17400, 5120, 5)])
+def test_five_to_eight_rows_tile_counts(oracle_mod, N, K, M):
+    """Five to eight resident activation rows over tile counts 1, 3 (odd), 513,
+    129 and N below one tile (one group of 8 waves per workgroup), and over
+    2176, 2049 and 2175 tiles of matrices of 16 MB or more (two subgroups per
+    workgroup, where the second walks padding tiles when it owns fewer):
+    every row bit-identical to its own M=1 launch, a canary row past M
+    untouched, all columns (or a sample holding the last one) within
+    tolerance of the oracle."""
+    A, codes, d, packed = _case(47, N, K, M, salt=N * 3 + K + M)
+    Bd = dev_u8(packed)
+    got = q2_0_gpu(A, Bd, N, K, extra_rows=1)
+    assert np.all(got[M] == CANARY)
+    got = got[:M]
+    for m in range(M):
+        assert np.array_equal(got[m:m + 1], q2_0_gpu(A[m:m + 1], Bd, N, K, single=True)), m
+    cols = np.arange(N) if N <= 400 else np.union1d(gen.rng(947, N, K).choice(N, 256, replace=False), [N - 1])
+    check_parity(got[:, cols], oracle_mod.q2_0_gemv(A, codes[cols], d[cols]), f"q2_0 {N}x{K} M={M}")

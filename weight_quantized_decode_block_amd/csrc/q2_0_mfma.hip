@@ -371,18 +371,19 @@ __global__ __launch_bounds__(kThreads) void q2_0_phase_kernel(const uint16_t *__
 // ---------------------------------------------------------------------------
 // Resident-activation kernel (the usual case): per-wave block pairs.
 // ---------------------------------------------------------------------------
-// LDS: [zero rows: 256][partial tiles: 2 x 8 slots x 2 x MMAX x 8 floats]
-// [seeds: nb x 8 floats][A: M rows, pitch 2K + 16].
-template <int MMAX>
+// LDS: [zero rows: 256][partial tiles, per subgroup: 2 x 8 slots x 2 x MMAX x 8 floats]
+// [seeds, per subgroup: nb x 8 floats][A: M rows, pitch 2K + 16].
+template <int MMAX, int SG = 1>
 struct PairLayout {
   static constexpr int kZero = 0;
   static constexpr int kPart = kZero + 256;
-  static constexpr int kFixed = kPart + 2 * kSlots8 * 2 * MMAX * kRows * 4;
+  static constexpr int kPartBytes = 2 * kSlots8 * 2 * MMAX * kRows * 4;  // one subgroup's
+  static constexpr int kFixed = kPart + SG * kPartBytes;
 };
 
-template <int MMAX>
+template <int MMAX, int SG = 1>
 constexpr size_t pair_lds_bytes(uint32_t M, uint32_t K) {
-  return (size_t)PairLayout<MMAX>::kFixed + (size_t)(K >> 7) * 32u + (size_t)M * (2u * K + 16u);
+  return (size_t)PairLayout<MMAX, SG>::kFixed + (size_t)SG * (K >> 7) * 32u + (size_t)M * (2u * K + 16u);
 }
 
 // One block pair's bytes for this lane: the aligned 3-dword window holding
@@ -398,23 +399,34 @@ struct PairRegs {
 // Weight bytes go straight from memory to the lanes that use them (buffer
 // loads bounded by the matrix size): lane (h, r, g) reads 12 bytes at
 // 68p + 32h + 8g of weight row r and 2 bytes (the scale) at 68p + 34h.
-template <int MMAX, int NW, int DEPTH, int UA, bool WFIRST>
-__global__ __launch_bounds__(64 * NW) void q2_0_pairs_kernel(const uint16_t *__restrict__ A,
-                                                             const uint8_t *__restrict__ B,
-                                                             uint16_t *__restrict__ C, uint32_t N, uint32_t K,
-                                                             uint32_t M) {
-  using L = PairLayout<MMAX>;
+//
+// SG = 2 runs two such groups of NW waves in one workgroup over one LDS copy
+// of the activations: subgroup s walks the tiles of virtual workgroup
+// 2 blockIdx.x + s of a grid of 2 gridDim.x, with its own partials and
+// seeds, so every output is computed as with SG = 1.  The once-per-tile
+// barrier is shared, so both subgroups walk as many tiles as subgroup 0; the
+// tiles past subgroup 1's own count load in bounds (the last tile) and
+// neither compute nor store.
+template <int MMAX, int NW, int DEPTH, int UA, bool WFIRST, int SG = 1>
+__global__ __launch_bounds__(64 * NW * SG) void q2_0_pairs_kernel(const uint16_t *__restrict__ A,
+                                                                  const uint8_t *__restrict__ B,
+                                                                  uint16_t *__restrict__ C, uint32_t N, uint32_t K,
+                                                                  uint32_t M) {
+  using L = PairLayout<MMAX, SG>;
   constexpr int NF = MMAX < 4 ? MMAX : 4;  // accumulator rows that can hold outputs
   constexpr int NACC = kSlots8 / NW;       // accumulation slots per wave
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  static_assert(SG == 1 || (SG == 2 && NW == 8), "one or two subgroups of 8 waves");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63u;
-  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t wave = __builtin_amdgcn_readfirstlane((tid >> 6) & (uint32_t)(NW - 1));
+  const uint32_t sg = SG == 1 ? 0u : __builtin_amdgcn_readfirstlane(tid / (64u * NW));
+  const uint32_t ltid = tid - sg * (64u * NW);  // thread index within the subgroup
   const uint32_t i = lane & 15u, g = lane >> 4;
   const uint32_t h = i >> 3, rw = i & 7u;  // MFMA column i = (block half h, weight row rw)
   const uint32_t nb = K >> 7, npairs = nb >> 1;
-  const uint32_t a_off = L::kFixed + nb * 32u;
+  const uint32_t a_off = L::kFixed + (uint32_t)SG * nb * 32u;
 
   // Activation staging, UA chunks per thread per round: the launcher picks UA
   // so that one round usually holds all of A.  Chunk c of A (16 bytes, row
@@ -428,7 +440,7 @@ __global__ __launch_bounds__(64 * NW) void q2_0_pairs_kernel(const uint16_t *__r
   auto a_load = [&](uint32_t base) {
 #pragma unroll
     for (int u = 0; u < UA; ++u) {
-      const uint32_t c = base + (uint32_t)u * (64u * NW) + tid;
+      const uint32_t c = base + (uint32_t)u * (64u * NW * SG) + tid;
       const bool in = c < total;
       const uint32_t cc = in ? c : 0u;
       uint32_t m = 0;
@@ -446,13 +458,16 @@ __global__ __launch_bounds__(64 * NW) void q2_0_pairs_kernel(const uint16_t *__r
 
   const uint32_t rb = nb * kBlockBytes;
   const uint32_t ntiles = N >= (uint32_t)kRows ? (N + kRows - 1u) / kRows : 1u;
-  const uint32_t my_tiles = (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x;
+  const uint32_t gx = gridDim.x * (uint32_t)SG, bx = blockIdx.x * (uint32_t)SG + sg;
+  const uint32_t b0 = blockIdx.x * (uint32_t)SG;             // subgroup 0's virtual workgroup
+  const uint32_t my_tiles = (ntiles - b0 + gx - 1) / gx;     // tiles walked (and barriers) by every wave
+  const uint32_t own_tiles = (ntiles - bx + gx - 1) / gx;    // tiles that are this subgroup's own
   // pairs of a tile owned by this wave: wave, wave + NW, ...  A wave that
   // owns none (K = 1024, NW = 8) still runs one unit per tile that computes
   // nothing, so every wave meets the once-per-tile barrier.
   const uint32_t upw = npairs > wave ? (npairs - wave + NW - 1) / NW : 1u;
   const uint32_t nq = my_tiles * upw;
-  const uint32_t seed_off = L::kFixed;
+  const uint32_t seed_off = L::kFixed + sg * nb * 32u;
   const uint32_t a_pitch = 2u * K + 16u;
 
   auto zero_rows = [&]() {
@@ -475,9 +490,9 @@ __global__ __launch_bounds__(64 * NW) void q2_0_pairs_kernel(const uint16_t *__r
   struct Cursor {
     uint32_t q, u, j, row;  // unit, pair index within the tile, tile index, tile's first row
   };
-  const uint32_t row_step = (uint32_t)kRows * gridDim.x;
+  const uint32_t row_step = (uint32_t)kRows * gx;
   const uint32_t row_last = N >= (uint32_t)kRows ? N - (uint32_t)kRows : 0u;
-  auto first_row = [&]() { return N >= (uint32_t)kRows ? min(blockIdx.x * (uint32_t)kRows, row_last) : 0u; };
+  auto first_row = [&]() { return N >= (uint32_t)kRows ? min(bx * (uint32_t)kRows, row_last) : 0u; };
   auto advance = [&](Cursor &c) {
     ++c.q;
     if (++c.u == upw) {
@@ -506,7 +521,7 @@ __global__ __launch_bounds__(64 * NW) void q2_0_pairs_kernel(const uint16_t *__r
   // the 8 code bytes sit at byte 2 (h = 0) or 4 (h = 1) of the window
   const uint32_t sel = h ? 0x07060504u : 0x05040302u;
   const bool lane_out = (g >> 1) == h;
-  float *part = reinterpret_cast<float *>(lds + L::kPart);  // [tile parity][slot][half][m][r]
+  float *part = reinterpret_cast<float *>(lds + L::kPart + sg * (uint32_t)L::kPartBytes);  // [tile parity][slot][half][m][r]
 
   // ---- prologue: A into LDS (permuted) while the first DEPTH pairs are in flight
   PairRegs ring[DEPTH];
@@ -528,7 +543,7 @@ __global__ __launch_bounds__(64 * NW) void q2_0_pairs_kernel(const uint16_t *__r
       zero_rows();
     }
     a_store();
-    for (uint32_t base = UA * (64u * NW); base < total; base += UA * (64u * NW)) {
+    for (uint32_t base = UA * (64u * NW * SG); base < total; base += UA * (64u * NW * SG)) {
       a_load(base);
       a_store();
     }
@@ -575,7 +590,8 @@ __global__ __launch_bounds__(64 * NW) void q2_0_pairs_kernel(const uint16_t *__r
   auto step = [&](PairRegs &r) {
     const uint32_t j = cc.j, u = cc.u, row = cc.row;
     const uint32_t p = wave + NW * u;
-    if (p < npairs) {
+    const bool own = SG == 1 || j < own_tiles;
+    if (p < npairs && own) {
       if (NACC == 1 || (u & 1u) == 0u)
         unit(r, p, j == 0u, acc[0]);
       else
@@ -599,8 +615,8 @@ __global__ __launch_bounds__(64 * NW) void q2_0_pairs_kernel(const uint16_t *__r
 #pragma unroll
       for (int k = 0; k < NACC; ++k) acc[k] = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
       __syncthreads();
-      if (tid < M * (uint32_t)kRows) {
-        const uint32_t m = tid >> 3, col = tid & 7u;
+      if (ltid < M * (uint32_t)kRows && own) {
+        const uint32_t m = ltid >> 3, col = ltid & 7u;
         const uint32_t n = row + col;
         if (n < N) {
           const float *pp = part + (par * kSlots8 * 2u * MMAX + m) * kRows + col;
@@ -713,8 +729,24 @@ hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32
   // one beyond (eight rows of activations leave LDS for one).
   constexpr int kDepth = 3;  // weights first
   constexpr int kMaxPerCu = MMAX <= 4 ? 2 : 1;
-  const size_t lds = pair_lds_bytes<MMAX>(M, K);
   const bool bounded = (uint64_t)N * (K >> 7) * kBlockBytes < (1ull << 32);  // buffer-load range
+  const bool big = (uint64_t)N * (K >> 7) * kBlockBytes >= (16ull << 20);
+  // Five to eight rows of a matrix of 16 MB or more: two subgroups of 8 waves
+  // per workgroup over one copy of the activations (measured on MI355X,
+  // N = 17408, K = 5120: M = 8 12.45 -> 11.46 us, M = 5 12.54 -> 11.70; at
+  // N = K = 5120 one group stays faster, 6.74 against 7.31).
+  if constexpr (MMAX == 8) {
+    const size_t lds2 = pair_lds_bytes<8, 2>(M, K);
+    if (big && lds2 <= kLdsMax && bounded) {
+      const uint32_t pt = (M * (K >> 3) + 1023u) / 1024u;
+      const uint32_t half = (ntiles + 1u) / 2u;
+      if (pt <= 2) return launch_persistent<q2_0_pairs_kernel<8, NW, kDepth, 2, true, 2>>(1024, lds2, 1, half, stream, a, b, c, N, K, M);
+      if (pt <= 3) return launch_persistent<q2_0_pairs_kernel<8, NW, kDepth, 3, true, 2>>(1024, lds2, 1, half, stream, a, b, c, N, K, M);
+      if (pt <= 5) return launch_persistent<q2_0_pairs_kernel<8, NW, kDepth, 5, true, 2>>(1024, lds2, 1, half, stream, a, b, c, N, K, M);
+      return launch_persistent<q2_0_pairs_kernel<8, NW, kDepth, 10, true, 2>>(1024, lds2, 1, half, stream, a, b, c, N, K, M);
+    }
+  }
+  const size_t lds = pair_lds_bytes<MMAX>(M, K);
   if (lds <= kLdsMax && bounded) {  // activations fit in LDS: the pairs kernel
     // activation chunks per thread for one staging round covering all of A
     const uint32_t per_thread = (M * (K >> 3) + 64 * NW - 1) / (64 * NW);
@@ -726,7 +758,6 @@ hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32
     // M = 2: 5.53 -> 4.86 us, M = 4: 6.68 -> 6.30); weights first for 5..8
     // rows (even at M = 8) and for batched rows of larger matrices (N = 17408,
     // M = 8: 12.5 against 13.7 us).
-    const bool big = (uint64_t)N * (K >> 7) * kBlockBytes >= (16ull << 20);
     const bool wfirst = M > 4 || (M > 1 && big);
     // Staging chunks per thread: the smallest of 2, 3, 4, 5 and 10 that
     // covers A in one round (idle chunk slots cost loads and registers before
