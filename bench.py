@@ -414,7 +414,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profile(kern_src, "q2_0_gemv_kernel_m1_5120x5120"),
-                     "kernel": "q2_0_pairs_kernel<1, 8, 2, 2, false, 1>", "kernel_us_avg": head["us_per_call"]},
+                     "kernel": "q2_0_pairs_kernel<1, 8, 2, 2, false, 1, true>", "kernel_us_avg": head["us_per_call"]},
         "cpu_baseline": cpu,
         "read_ceiling": {"us_per_call": head["read_ceiling_us"], "gbs": head["read_ceiling_gbs"],
                          "frac": head["frac_read_ceiling"],

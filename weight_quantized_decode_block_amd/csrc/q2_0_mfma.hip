@@ -387,7 +387,10 @@ constexpr size_t pair_lds_bytes(uint32_t M, uint32_t K) {
 }
 
 // One block pair's bytes for this lane: the aligned 3-dword window holding
-// its 8 code bytes and the dword holding its fp16 scale (low half).
+// its 8 code bytes and, with SEPD, the dword holding its fp16 scale (low
+// half).  Without SEPD the scale comes from the window of lane g = 0 of the
+// same column, which starts at the half's scale (first block) or two bytes
+// before it (second block), through one cross-lane permute.
 struct PairRegs {
   u32x3_t w;
   uint32_t d;
@@ -398,7 +401,8 @@ struct PairRegs {
 // accumulator per slot it owns, so the sums are those of the per-phase kernel.
 // Weight bytes go straight from memory to the lanes that use them (buffer
 // loads bounded by the matrix size): lane (h, r, g) reads 12 bytes at
-// 68p + 32h + 8g of weight row r and 2 bytes (the scale) at 68p + 34h.
+// 68p + 32h + 8g of weight row r and, with SEPD, 2 bytes (the scale) at
+// 68p + 34h; without SEPD the scale is taken from lane (h, r, 0)'s 12 bytes.
 //
 // SG = 2 runs two such groups of NW waves in one workgroup over one LDS copy
 // of the activations: subgroup s walks the tiles of virtual workgroup
@@ -407,7 +411,7 @@ struct PairRegs {
 // barrier is shared, so both subgroups walk as many tiles as subgroup 0; the
 // tiles past subgroup 1's own count load in bounds (the last tile) and
 // neither compute nor store.
-template <int MMAX, int NW, int DEPTH, int UA, bool WFIRST, int SG = 1>
+template <int MMAX, int NW, int DEPTH, int UA, bool WFIRST, int SG = 1, bool SEPD = false>
 __global__ __launch_bounds__(64 * NW * SG) void q2_0_pairs_kernel(const uint16_t *__restrict__ A,
                                                                   const uint8_t *__restrict__ B,
                                                                   uint16_t *__restrict__ C, uint32_t N, uint32_t K,
@@ -481,7 +485,7 @@ __global__ __launch_bounds__(64 * NW * SG) void q2_0_pairs_kernel(const uint16_t
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(B), (short)0, (int)(N * rb), 0x00020000);
   const uint32_t row_off = min(rw, N - 1u) * rb;  // rows past N (N < 8) re-read row N - 1
   const uint32_t w_voff = row_off + 32u * h + 8u * g;
-  const uint32_t d_voff = row_off + 34u * h;
+  const uint32_t d_voff = row_off + 34u * h;  // used with SEPD
   // Unit q of this wave is pair wave + NW*u of tile j (q = j * upw + u).
   // Two wave-uniform cursors walk the units in order, one for the loads
   // (DEPTH units ahead) and one for the compute, so the per-unit bookkeeping
@@ -508,7 +512,11 @@ __global__ __launch_bounds__(64 * NW * SG) void q2_0_pairs_kernel(const uint16_t
     const uint32_t soff = ld.q < nq ? ld.row * rb + 68u * p : soff_first;
     PairRegs r;
     r.w = __builtin_amdgcn_raw_buffer_load_b96(wrsrc, w_voff, soff, 0);
-    r.d = __builtin_amdgcn_raw_buffer_load_b16(wrsrc, d_voff, soff, 0);
+    if constexpr (SEPD) {
+      r.d = __builtin_amdgcn_raw_buffer_load_b16(wrsrc, d_voff, soff, 0);
+    } else {
+      r.d = 0u;
+    }
     advance(ld);
     return r;
   };
@@ -570,7 +578,12 @@ __global__ __launch_bounds__(64 * NW * SG) void q2_0_pairs_kernel(const uint16_t
     }
     const uint32_t w0 = __builtin_amdgcn_perm(r.w.y, r.w.x, sel);
     const uint32_t w1 = __builtin_amdgcn_perm(r.w.z, r.w.y, sel);
-    const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)r.d);
+    uint32_t dbits = r.d;
+    if constexpr (!SEPD) {
+      const uint32_t own_d = h ? (r.w.x >> 16) : (r.w.x & 0xFFFFu);  // meaningful on lanes g = 0
+      dbits = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(i << 2), (int)own_d);
+    }
+    const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)dbits);
     bf16x8_t b0, b1, b2, b3;
     decode_word(w0, b0, b1);
     decode_word(w1, b2, b3);
@@ -763,6 +776,22 @@ hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32
     // covers A in one round (idle chunk slots cost loads and registers before
     // the staging barrier: N = K = 5120 M = 2: 4.86 -> 4.71 us, N = 5120
     // K = 17408 M = 1: 9.92 -> 9.33).
+    //
+    // The scale by its own load for one row under 16 MB, else from the code
+    // window of the column's first lane (the same bits; measured on MI355X,
+    // interleaved A/B: N = K = 5120, M = 1 4.47 against 4.49 us with the
+    // permute, N = 256 K = 1024 2.33 against 2.36; with the permute N = 5120
+    // K = 17408 M = 1 9.32 -> 8.92 us, N = K = 5120 M = 2 4.70 -> 4.62, M = 8
+    // 6.71 -> 6.61).
+    if constexpr (MMAX == 1) {
+      if (!big) {
+        if (per_thread <= 2) return launch_persistent<q2_0_pairs_kernel<1, NW, 2, 2, false, 1, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
+        if (per_thread <= 3) return launch_persistent<q2_0_pairs_kernel<1, NW, 2, 3, false, 1, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
+        if (per_thread <= 4) return launch_persistent<q2_0_pairs_kernel<1, NW, 2, 4, false, 1, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
+        if (per_thread <= 5) return launch_persistent<q2_0_pairs_kernel<1, NW, 2, 5, false, 1, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
+        return launch_persistent<q2_0_pairs_kernel<1, NW, 2, 10, false, 1, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
+      }
+    }
     if (!wfirst) {
       if constexpr (MMAX <= 4) {
         if (per_thread <= 2) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 2, false>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
