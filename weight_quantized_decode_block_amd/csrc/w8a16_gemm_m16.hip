@@ -381,14 +381,18 @@ __global__ __launch_bounds__(kThreads) void w8a16_units_kernel(const uint16_t *_
     const uint32_t b = min(wave + kWaves * ld.u, nb - 1u);
     const uint32_t n0 = live ? ld.n0 : r0;
     const uint32_t row = n0 + i;
-    const uint32_t voff = row < r1 ? row * K + w_lane : kPastEnd;
+    // past the wave's last unit the loads fall outside the buffer (the range
+    // check returns zeros without a memory access; re-reading the first
+    // tile's weights, long evicted from L2 at large N, cost 10-15 % more HBM
+    // traffic and the wait for it: N = 17408, K = 5120, M = 1 19.1 -> 18.2 us)
+    const uint32_t voff = (live && row < r1) ? row * K + w_lane : kPastEnd;
     const uint32_t soff = 128u * b;
     UnitRegs r;
     r.w0 = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, voff, soff, 0);
     r.w1 = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, voff + 16u, soff, 0);
     // the scale of this lane's own row: a tile need not sit inside one 128-row scale group
     const uint32_t srow = (row < r1 ? row : r1 - 1u) >> 7;
-    r.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srsrc, srow * nb * 4u, 4u * b, 0));
+    r.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srsrc, live ? srow * nb * 4u : kPastEnd, 4u * b, 0));
     advance(ld);
     return r;
   };
