@@ -181,7 +181,12 @@ def test_pages_test_vectors_within_bound(oracle_mod):
 
 # --------------------------------------------------------------- brute force
 def _emulate_row(a_bits, codes_row, d_row):
-    """Step-by-step float32 emulation of one output (tiny inputs only)."""
+    """Step-by-step float32 emulation of one output (tiny inputs only).
+
+    This restates the oracle's own loop in numpy, so it checks the C side's
+    plumbing (codecs, indexing, block of each k) on random inputs, not the
+    summation order; the order is pinned by the hand-derived examples in
+    test_oracle_order.py."""
     acc = np.float32(0.0)
     a = gen.bf16_values(a_bits)
     dv = d_row.view(np.float16).astype(np.float32)
