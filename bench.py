@@ -215,22 +215,74 @@ def sweep_list():
 
 
 # ------------------------------------------------------------------- timing
-def graph_group(steps: int) -> int:
-    """Steps per captured graph: the largest divisor of `steps` up to 128, so
-    that exactly `steps` steps run in the timed region."""
-    return max(d for d in range(1, min(steps, 128) + 1) if steps % d == 0)
+def timed_plan(R: int, steps: int):
+    """How the timed region walks the ring of R weight copies: `full` replays
+    of a graph over copies 0..R-1, then one graph over copies 0..rest-1
+    (steps = full * R + rest, exactly).  An untimed replay of the full-ring
+    graph runs just before, so every timed step reads the copy that was last
+    read R steps earlier: R - 1 other copies in between."""
+    full, rest = divmod(steps, R)
+    return full, rest
+
+
+def timed_traffic(R: int, nbytes: int, steps: int):
+    """Weight bytes of the timed region: distinct copies touched, and the
+    fewest bytes of other weight copies read between two reads of one copy
+    (the reuse distance; above the 256 MB on-die cache it is a cold read)."""
+    distinct = min(steps, R)
+    return {"distinct_copies": distinct, "distinct_bytes": distinct * nbytes,
+            "reuse_distance_bytes": (R - 1) * nbytes}
+
+
+def _capture(torch, wqd, wl, copies):
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for i in copies:
+                wl.call(wqd, i)
+    torch.cuda.synchronize()
+    return graph
+
+
+_SLEEP_CYCLES = None
+
+
+def _gpu_pre_delay(torch):
+    """Keep the GPU busy for about 0.3 ms before the timed region opens, so
+    that the host has enqueued the timed launches by then and the host's
+    launch cost stays out of the measured device time.  The spin kernel is
+    torch's own bounded one; its length is calibrated once with events."""
+    global _SLEEP_CYCLES
+    if _SLEEP_CYCLES is None:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        probe = 1_000_000
+        torch.cuda._sleep(probe)  # first launch loads the kernel
+        torch.cuda.synchronize()
+        e0.record()
+        torch.cuda._sleep(probe)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = max(e0.elapsed_time(e1), 1e-3)
+        _SLEEP_CYCLES = int(min(probe * 0.3 / ms, 2e9))
+    torch.cuda._sleep(_SLEEP_CYCLES)
 
 
 def time_workload(torch, wqd, wl, steps, warmup):
     """Milliseconds per step over the timed region, HIP events recorded on the
     stream the kernels run on.
 
-    Returns (graph, eager).  graph: `steps` steps replayed from HIP graphs of
-    G = graph_group(steps) captured steps each (each step of a graph uses its
-    own ring copy), which is how a decode loop issues fixed-shape launches and
-    leaves only the GPU's own per-dispatch cost between kernels.  eager: the
-    same steps launched one by one from Python, which adds the host's launch
-    cost (several microseconds per call) whenever that exceeds the kernel."""
+    Returns (graph, eager).  graph: `steps` steps replayed from captured HIP
+    graphs that walk the weight ring in order (timed_plan), which is how a
+    decode loop issues fixed-shape launches and leaves only the GPU's own
+    per-dispatch cost between kernels; every timed step reads a copy last read
+    R steps before, whatever `steps` is.  eager: the same number of steps
+    launched one by one from Python, continuing around the ring, which adds
+    the host's launch cost (several microseconds per call) whenever that
+    exceeds the kernel."""
+    R = wl.R
     for i in range(warmup):
         wl.call(wqd, i)
     torch.cuda.synchronize()
@@ -243,47 +295,73 @@ def time_workload(torch, wqd, wl, steps, warmup):
     torch.cuda.synchronize()
     eager = t0.elapsed_time(t1) / steps
 
-    G = graph_group(steps)
-    side = torch.cuda.Stream()
-    side.wait_stream(stream)
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(side):
-        with torch.cuda.graph(graph, stream=side):
-            for i in range(G):
-                wl.call(wqd, warmup + i)
-    torch.cuda.synchronize()
-    graph.replay()  # one untimed replay
-    torch.cuda.synchronize()
+    full, rest = timed_plan(R, steps)
+    g_full = _capture(torch, wqd, wl, range(R))
+    g_rest = _capture(torch, wqd, wl, range(rest)) if rest else None
+    g_full.replay()  # untimed: the whole ring once, ending at copy R - 1
+    _gpu_pre_delay(torch)
     t0.record(stream)
-    for _ in range(steps // G):
-        graph.replay()
+    for _ in range(full):
+        g_full.replay()
+    if g_rest is not None:
+        g_rest.replay()
     t1.record(stream)
     torch.cuda.synchronize()
-    del graph
+    del g_full, g_rest
     return t0.elapsed_time(t1) / steps, eager
 
 
-def cpu_threads() -> int:
+def cpu_info():
+    """Host facts reported beside the CPU baseline."""
+    model = None
     try:
-        n = len(os.sched_getaffinity(0))
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
     except Exception:
-        n = os.cpu_count() or 1
-    return max(1, min(16, n))
+        usable = os.cpu_count() or 1
+    return {"cpu_model": model, "nproc": os.cpu_count(), "usable_cpus": usable}
 
 
-def traffic_from_profile(kernel_src: str, name: str):
-    """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel source (else None)."""
+# CPU threads of one GPU's share of the GPU host: the oracle's worker threads
+# are capped there, whatever the host's core count.
+GPU_SHARE_CPUS = 16
+
+
+def cpu_threads() -> int:
+    return max(1, min(GPU_SHARE_CPUS, cpu_info()["usable_cpus"]))
+
+
+# The headline's kernel and the committed rocprofv3 summary that covers it.
+HEADLINE_KERNEL = {"name": "q2_0_pairs_kernel<1, 8, 2, 2, false, 1, true>", "source": "q2_0_mfma.hip",
+                   "profile": "q2_0_gemv_kernel_m1_5120x5120"}
+
+
+def profile_facts(kernel_src: str, name: str) -> dict:
+    """HBM bytes per launch and kernel-trace average from the committed
+    rocprofv3 summary, if it was taken on the current kernel source (else
+    empty)."""
     prof = os.path.join(ROOT, "profiles", f"{name}.md")
     if not os.path.exists(prof):
-        return None
+        return {}
     text = open(prof).read()
     sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
     m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    if not m_sha or m_sha.group(1) != sha:
+        return {}
+    out = {}
     m_t = re.search(r"traffic_bytes_per_launch:\s*([0-9.]+)", text)
-    if not m_sha or not m_t or m_sha.group(1) != sha:
-        return None
-    return float(m_t.group(1))
+    if m_t:
+        out["traffic"] = float(m_t.group(1))
+    m_u = re.search(r"trace_avg_us:\s*([0-9.]+)", text)
+    if m_u:
+        out["trace_us"] = float(m_u.group(1))
+    return out
 
 
 def main():
@@ -337,6 +415,7 @@ def main():
                "read_ceiling_gbs": round(probe.nbytes / (read_ms * 1e-3) / 1e9, 1)}
         res["frac_hbm"] = round(res["gbs"] / HBM_PEAK_GBS, 4)
         res["frac_read_ceiling"] = round(read_ms / step_ms, 4)
+        res["timed"] = timed_traffic(wl.R, wl.bytes, steps)
         log(f"[bench] {name}: {res['us_per_call']} us/call, {res['gbs']} GB/s, "
             f"{100 * res['frac_hbm']:.1f}% of HBM peak (eager launches: {res['us_per_call_eager']} us/call); "
             f"plain read of the same ring {res['read_ceiling_us']} us ({res['read_ceiling_gbs']} GB/s)")
@@ -366,19 +445,29 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
+        def oracle_rate(nthr, seconds):
+            calls, t0 = 0, time.perf_counter()
+            while True:
+                wl.oracle_call(oracle, nthr)
+                calls += 1
+                el = time.perf_counter() - t0
+                if el >= seconds:
+                    return calls, el
+
+        info = cpu_info()
         nthr = cpu_threads()
-        calls, t0 = 0, time.perf_counter()
-        while True:
-            wl.oracle_call(oracle, nthr)
-            calls += 1
-            el = time.perf_counter() - t0
-            if el >= args.cpu_seconds:
-                break
+        calls, el = oracle_rate(nthr, args.cpu_seconds)
+        calls1, el1 = oracle_rate(1, max(1.0, args.cpu_seconds / 3))
         cpu = {"value": round(wl.bytes * calls / el / 1e9, 4), "unit": "GB/s", "cores": nthr,
                "kind": "oracle",
                "sample": f"oracle_q2_0_gemv over the whole N=K=5120 M=1 workload (ring copy 0), "
-                         f"{calls} calls in {el:.2f} s on {nthr} threads"}
-        log(f"[bench] cpu oracle: {cpu['value']} GB/s ({calls} calls, {el:.1f}s, {nthr} threads)")
+                         f"{calls} calls in {el:.2f} s on {nthr} threads (one GPU's share of the host's CPUs); "
+                         f"1 thread: {calls1} calls in {el1:.2f} s",
+               "value_1_core": round(wl.bytes * calls1 / el1 / 1e9, 4),
+               "us_per_call": round(el / calls * 1e6, 1), "us_per_call_1_core": round(el1 / calls1 * 1e6, 1),
+               **info}
+        log(f"[bench] cpu oracle: {cpu['value']} GB/s ({calls} calls, {el:.1f}s, {nthr} threads); "
+            f"1 thread {cpu['value_1_core']} GB/s; {info}")
     wl.free()
     torch.cuda.empty_cache()
 
@@ -390,8 +479,10 @@ def main():
             torch.cuda.empty_cache()
             sweep.append(r2)
 
-    kern_src = os.path.join(ROOT, "weight_quantized_decode_block_amd", "csrc", "q2_0_mfma.hip")
-    achieved = head["gbs"]  # one dispatch per step, back to back: step time = launch duration
+    kern_src = os.path.join(ROOT, "weight_quantized_decode_block_amd", "csrc", HEADLINE_KERNEL["source"])
+    prof = profile_facts(kern_src, HEADLINE_KERNEL["profile"])
+    achieved = head["gbs"]  # one dispatch per step, back to back: step time = average launch duration
+    tt = head["timed"]
     line = {
         "metric": METRIC,
         "value": head["gbs"],
@@ -406,15 +497,25 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "Q2_0 ternary GEMV M=1 N=5120 K=5120 group=128, bf16 activations, "
-                               f"weights cold-cycled through {head['ring']} distinct copies "
-                               f"({head['ring'] * head['bytes_per_call'] / 2**20:.0f} MiB), "
-                               f"launches replayed from HIP graphs of {graph_group(args.steps)} steps",
+                               f"weights cycled in order through a ring of {head['ring']} distinct copies "
+                               f"({head['ring'] * head['bytes_per_call'] / 2**20:.0f} MiB); the timed "
+                               f"{args.steps} steps touch {tt['distinct_copies']} distinct copies "
+                               f"({tt['distinct_bytes'] / 2**20:.0f} MiB) and every timed read of a copy comes "
+                               f"{tt['reuse_distance_bytes'] / 2**20:.0f} MiB of other weight copies after its "
+                               f"previous read (above the 256 MB on-die cache); launches replayed from HIP graphs",
                    "bytes_per_call": head["bytes_per_call"], "frac_hbm_peak": head["frac_hbm"],
-                   "us_per_call": head["us_per_call"], "us_per_call_eager": head["us_per_call_eager"]},
+                   "us_per_call": head["us_per_call"], "us_per_call_eager": head["us_per_call_eager"],
+                   "timed": tt},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_from_profile(kern_src, "q2_0_gemv_kernel_m1_5120x5120"),
-                     "kernel": "q2_0_pairs_kernel<1, 8, 2, 2, false, 1, true>", "kernel_us_avg": head["us_per_call"]},
+                     "traffic": prof.get("traffic"),
+                     "kernel": HEADLINE_KERNEL["name"],
+                     "launch_us_avg_events": head["us_per_call"],
+                     "trace_us_avg": prof.get("trace_us"),
+                     "note": "achieved = algorithmic weight bytes per launch / average launch duration from HIP "
+                             "events around graph-replayed launches on the kernel's stream; trace_us_avg is the "
+                             "rocprofv3 kernel-trace average of the committed profile (null if the kernel source "
+                             "changed since)"},
         "cpu_baseline": cpu,
         "read_ceiling": {"us_per_call": head["read_ceiling_us"], "gbs": head["read_ceiling_gbs"],
                          "frac": head["frac_read_ceiling"],

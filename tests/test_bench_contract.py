@@ -1,7 +1,8 @@
 """bench.py's contract, checked without a GPU: the workloads it times cover
 the benchmark configurations (Q2_0 M=1 and N=K=5120 batched rows, W8A16
 M in {1, 8, 16}, the FFN shapes at M in {1, 8, 16, 32}), weight rings larger
-than the 256 MB on-die cache, exactly K timed steps, and one GPU only."""
+than the 256 MB on-die cache, exactly K timed steps that each read a cold
+copy whatever K is, and one GPU only."""
 import importlib.util
 import os
 import subprocess
@@ -43,11 +44,30 @@ def test_weight_rings_exceed_the_on_die_cache():
     assert b.fp8_bytes(5120, 5120) == 26220800
 
 
-def test_graph_group_times_exactly_the_requested_steps():
+def test_timed_plan_times_exactly_the_requested_steps():
     b = _bench()
-    for steps in (1, 5, 200, 1000, 2000, 997):
-        g = b.graph_group(steps)
-        assert 1 <= g <= 128 and steps % g == 0
+    for R in (8, 21, 23, 78):
+        for steps in (1, 5, 20, 200, 997, 1000, 2000):
+            full, rest = b.timed_plan(R, steps)
+            assert full * R + rest == steps and 0 <= rest < R
+
+
+def test_every_timed_read_is_cold_at_the_drivers_step_count():
+    """At --steps 20 --warmup 5 (and at the defaults), every timed read of a
+    weight copy follows more than 256 MiB of reads of other copies since that
+    copy's previous read, for every workload whose configuration asks for
+    cold-cycled weights (all but the 70 KB N=256, K=1024 latency case)."""
+    b = _bench()
+    for steps in (20, 2000, 997, 1):
+        for entry in [b.HEADLINE] + b.sweep_list():
+            name, cls, wid, N, K, M = entry
+            wl = cls(name, wid, N, K, M)
+            R = b.ring_size(wl.bytes)
+            t = b.timed_traffic(R, wl.bytes, steps)
+            assert t["distinct_copies"] == min(steps, R)
+            if (N, K) == (256, 1024):
+                continue
+            assert t["reuse_distance_bytes"] > 256 * 1024 * 1024, (name, steps, t)
 
 
 def test_more_than_one_gpu_is_refused():
