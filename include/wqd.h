@@ -51,6 +51,7 @@ extern "C" {
 #define WQD_Q2_0_GROUP         128  /* weights per block_q2_0 */
 #define WQD_Q2_0_BLOCK_BYTES   34   /* fp16 d (2 B) + 128 x 2-bit codes (32 B) */
 #define WQD_Q2_0_BATCHM_MAX_M  8    /* rows per batched launch */
+#define WQD_Q2_0_MAX_K         (1u << 24)  /* largest K the Q2_0 entry points take */
 #define WQD_W8A16_MAX_M        16   /* rows per W8A16 call (the MFMA M tile) */
 #define WQD_W8A16_BLOCK        128  /* K and N extent of one FP8 scale */
 
@@ -76,7 +77,8 @@ extern "C" {
  *   B      device, block_q2_0 [N][K/128], 4-byte aligned
  *   C      device, BF16 [N], 2-byte aligned
  *   N      >= 1 output columns
- *   K      >= 128, a multiple of 128
+ *   K      >= 128, a multiple of 128 (else WQD_EINVAL), at most
+ *          WQD_Q2_0_MAX_K (else WQD_EUNSUPPORTED)
  *   group  must be 128 (the block size; other values give WQD_EINVAL)
  *
  * Each output is an fp32 sum over k stored as BF16 (round to nearest even);
@@ -220,6 +222,35 @@ int q2_0_pack(const uint8_t *codes, const uint16_t *d_f16,
  */
 uint32_t q2_0_batchm_chunks(uint32_t M, uint32_t K, uint32_t N,
                             uint64_t *out3, uint32_t cap);
+
+/*
+ * Q2_0 row tiers.  The matrix-core kernel is compiled for launches of at most
+ * 1, 2, 4, 6 and 8 rows (WQD_Q2_0_TIER_WIDTHS, narrowest first); a launch of m
+ * rows runs on the narrowest compiled width that covers m.  Every width gives
+ * the same bits for a row (its arithmetic does not depend on the width), a
+ * narrower one only skips work for rows that are not there.  Widths 1 and 8
+ * are the base tiers (the page's single-row GEMV and its 8-row batched
+ * launch); 2, 4 and 6 are exact-row tiers, which the presence of the
+ * environment variable WQD_NO_EXACT_M_TIERS (any value, "0" included; read
+ * once per process) removes from the decision without unloading anything.
+ * Follows page "w4a16_gemv_tiers.rs": "Why this module exists" (a wider tier
+ * pays for rows that are not there), "Kill switch" and select_tier
+ * (narrowest present tier that covers m, none for m = 0).
+ *
+ * q2_0_select_tier - the pure decision: index into WQD_Q2_0_TIER_WIDTHS of the
+ *   narrowest width >= m whose bit is set in present_mask and that is allowed
+ *   (exact_m != 0 allows the exact-row tiers), or -1 when m = 0 or nothing
+ *   covers m.  Pure host code; no HIP call, no environment access.
+ * q2_0_tier_width - the width q2_0_gemv / q2_0_gemv_batchm launch m rows on
+ *   in this process (every width compiled, the switch as read), or 0 when the
+ *   matrix-core family cannot serve m (m = 0 or m > 8).  No HIP call.
+ * q2_0_exact_m_tiers_enabled - 1 unless WQD_NO_EXACT_M_TIERS is present.
+ */
+#define WQD_Q2_0_TIER_COUNT 5
+#define WQD_Q2_0_TIER_WIDTHS {1u, 2u, 4u, 6u, 8u}
+int q2_0_select_tier(uint32_t m, uint32_t present_mask, int exact_m);
+uint32_t q2_0_tier_width(uint32_t m);
+int q2_0_exact_m_tiers_enabled(void);
 
 /* Text of the last failing call on this thread ("" if none). */
 const char *wqd_last_error(void);

@@ -207,3 +207,44 @@ def test_five_to_eight_rows_tile_counts(oracle_mod, N, K, M):
         assert np.array_equal(got[m:m + 1], q2_0_gpu(A[m:m + 1], Bd, N, K, single=True)), m
     cols = np.arange(N) if N <= 400 else np.union1d(gen.rng(947, N, K).choice(N, 256, replace=False), [N - 1])
     check_parity(got[:, cols], oracle_mod.q2_0_gemv(A, codes[cols], d[cols]), f"q2_0 {N}x{K} M={M}")
+
+
+_TIER_CHILD = r"""
+import sys
+import numpy as np
+sys.path.insert(0, sys.argv[1]); sys.path.insert(0, sys.argv[1] + "/tests")
+from parity import q2_0_gpu
+from weight_quantized_decode_block_amd import inputs as gen, wqd
+assert not wqd.q2_0_exact_m_tiers_enabled()
+outs = {}
+for N, K, M in [(5120, 5120, 3), (5120, 5120, 5), (5120, 5120, 6), (333, 17408, 6), (17400, 5120, 5)]:
+    A = gen.activations(53, K, M, N + M)
+    codes, d = gen.q2_0_weights(53, N, K, N + M)
+    assert wqd.q2_0_tier_width(M) == 8
+    outs[f"{N}_{K}_{M}"] = q2_0_gpu(A, wqd.q2_0_pack(codes, d), N, K)
+np.savez(sys.argv[2], **outs)
+"""
+
+
+def test_exact_row_tiers_equal_base_tier_bits(tmp_path):
+    """The kill switch moves 3, 5 and 6 rows from the exact 4- and 6-row tiers
+    onto the 8-row tier (page "w4a16_gemv_tiers.rs", "Kill switch"); run in a
+    child process with the switch set, every output is bit-identical to this
+    process's exact-tier launch, over the resident-activation kernel, the
+    per-phase kernel (K = 17408) and the two-subgroup path (N = 17400)."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, WQD_NO_EXACT_M_TIERS="1")
+    out = tmp_path / "tiers.npz"
+    print("child: kill switch set, shapes 5120^2 M=3,5,6; 333x17408 M=6; 17400x5120 M=5", flush=True)
+    subprocess.run([sys.executable, "-c", _TIER_CHILD, root, str(out)], env=env, check=True, timeout=300)
+    base = np.load(out)
+    assert wqd.q2_0_exact_m_tiers_enabled()
+    for key in base.files:
+        N, K, M = map(int, key.split("_"))
+        assert wqd.q2_0_tier_width(M) in (4, 6)
+        A = gen.activations(53, K, M, N + M)
+        codes, d = gen.q2_0_weights(53, N, K, N + M)
+        got = q2_0_gpu(A, wqd.q2_0_pack(codes, d), N, K)
+        assert np.array_equal(got, base[key]), key

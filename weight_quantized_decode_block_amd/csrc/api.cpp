@@ -12,7 +12,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
-#include <mutex>
+#include <atomic>
 
 #include "../../include/wqd.h"
 #include "wqd_internal.h"
@@ -31,10 +31,10 @@ int fail(int code, const char *fmt, ...) {
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// 0 = not yet checked, 1 = gfx950, 2 = other architecture.
+// 0 = not yet checked, 1 = gfx950, 2 = other architecture.  Written once
+// per device (racing writers store the same value), read without a lock.
 constexpr int kMaxDevices = 64;
-int g_dev_state[kMaxDevices] = {0};
-std::mutex g_dev_mu;
+std::atomic<int> g_dev_state[kMaxDevices];
 
 // Confirms a current HIP device exists and is a gfx950 part (the only code
 // object this library carries).
@@ -42,39 +42,42 @@ int check_device(const char *fn) {
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess || dev < 0) {
-    int count = 0;
-    (void)hipGetDeviceCount(&count);
     (void)hipGetLastError();
     return fail(WQD_ENODEV, "%s: no usable HIP device (%s)", fn, hipGetErrorString(e));
   }
   if (dev >= kMaxDevices) return fail(WQD_ENODEV, "%s: device index %d too large", fn, dev);
-  std::lock_guard<std::mutex> lk(g_dev_mu);
-  if (g_dev_state[dev] == 0) {
+  int state = g_dev_state[dev].load(std::memory_order_acquire);
+  if (state == 0) {
     hipDeviceProp_t prop;
     e = hipGetDeviceProperties(&prop, dev);
     if (e != hipSuccess) return fail(WQD_EHIP, "%s: hipGetDeviceProperties: %s", fn, hipGetErrorString(e));
-    g_dev_state[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    state = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_dev_state[dev].store(state, std::memory_order_release);
   }
-  if (g_dev_state[dev] != 1)
+  if (state != 1)
     return fail(WQD_EUNSUPPORTED, "%s: device %d is not gfx950 (this library carries gfx950 code only)", fn, dev);
   return WQD_OK;
 }
 
-// Kernel choice for Q2_0.  The matrix-core kernel serves every K that is a
-// multiple of 1024; other K use the vector-ALU kernel.  The presence of
-// WQD_Q2_0_VALU (any value; read once per process) forces the vector-ALU
-// kernel everywhere, for A/B runs.  The choice depends only on K, never on M,
-// so batched rows stay bit-identical to M=1 rows; the two kernels differ from
-// each other only by fp32 rounding order.
-bool q2_0_use_valu(uint32_t K, uint32_t m) {
-  static const bool forced = std::getenv("WQD_Q2_0_VALU") != nullptr;
-  return forced || !wqd::q2_0_mfma_supports(K, m);
-}
+// Q2_0 matrix-core row tiers (include/wqd.h, WQD_Q2_0_TIER_WIDTHS): widths 1
+// and 8 are the base tiers, 2, 4 and 6 the exact-row tiers.
+constexpr uint32_t kTierWidths[WQD_Q2_0_TIER_COUNT] = WQD_Q2_0_TIER_WIDTHS;
+constexpr bool kTierExact[WQD_Q2_0_TIER_COUNT] = {false, true, true, true, false};
+constexpr uint32_t kTiersCompiled = (1u << WQD_Q2_0_TIER_COUNT) - 1u;
 
+// Kernel for Q2_0, chosen from K only (never M), so batched rows stay
+// bit-identical to M=1 rows: the matrix-core kernel when K is a multiple of
+// 1024, on the row tier q2_0_tier_width(m), else the vector-ALU kernel.  The
+// two kernels differ from each other only by fp32 rounding order; every tier
+// of the matrix-core kernel gives the same bits.  The presence of
+// WQD_Q2_0_VALU (any value; read once per process) forces the vector-ALU
+// kernel everywhere, for A/B runs.
 hipError_t launch_q2_0(const void *A, const void *B, void *C, uint32_t N, uint32_t K, uint32_t m,
                        hipStream_t stream) {
-  return q2_0_use_valu(K, m) ? wqd::launch_q2_0_valu(A, B, C, N, K, m, stream)
-                             : wqd::launch_q2_0_mfma(A, B, C, N, K, m, stream);
+  static const bool valu = std::getenv("WQD_Q2_0_VALU") != nullptr;
+  const uint32_t width = q2_0_tier_width(m);
+  if (!valu && width != 0 && wqd::q2_0_pairs_supports(K)) return wqd::launch_q2_0_pairs(A, B, C, N, K, m, width, stream);
+  return wqd::launch_q2_0_valu(A, B, C, N, K, m, stream);
 }
 
 int check_launch(const char *fn, hipError_t e) {
@@ -89,6 +92,7 @@ int validate_q2_0(const char *fn, const void *A, const void *B, void *C, uint32_
   if (group != WQD_Q2_0_GROUP) return fail(WQD_EINVAL, "%s: group=%u, only 128 is supported", fn, group);
   if (N == 0) return fail(WQD_EINVAL, "%s: N must be >= 1", fn);
   if (K == 0 || K % WQD_Q2_0_GROUP != 0) return fail(WQD_EINVAL, "%s: K=%u is not a positive multiple of 128", fn, K);
+  if (K > WQD_Q2_0_MAX_K) return fail(WQD_EUNSUPPORTED, "%s: K=%u above %u", fn, K, (unsigned)WQD_Q2_0_MAX_K);
   if (!aligned(A, 16)) return fail(WQD_EALIGN, "%s: A must be 16-byte aligned", fn);
   if (!aligned(B, 4)) return fail(WQD_EALIGN, "%s: B must be 4-byte aligned", fn);
   if (!aligned(C, 2)) return fail(WQD_EALIGN, "%s: C must be 2-byte aligned", fn);
@@ -135,6 +139,23 @@ constexpr uint32_t kN64Band = 4;
 extern "C" {
 
 const char *wqd_last_error(void) { return g_last_error; }
+
+int q2_0_select_tier(uint32_t m, uint32_t present_mask, int exact_m) {
+  if (m == 0) return -1;
+  for (int i = 0; i < WQD_Q2_0_TIER_COUNT; ++i)
+    if (kTierWidths[i] >= m && ((present_mask >> i) & 1u) && (exact_m || !kTierExact[i])) return i;
+  return -1;
+}
+
+int q2_0_exact_m_tiers_enabled(void) {
+  static const int on = std::getenv("WQD_NO_EXACT_M_TIERS") == nullptr ? 1 : 0;
+  return on;
+}
+
+uint32_t q2_0_tier_width(uint32_t m) {
+  const int i = q2_0_select_tier(m, kTiersCompiled, q2_0_exact_m_tiers_enabled());
+  return i < 0 ? 0u : kTierWidths[i];
+}
 
 size_t q2_0_packed_bytes(uint32_t N, uint32_t K) {
   if (K % WQD_Q2_0_GROUP != 0) return 0;

@@ -736,19 +736,21 @@ hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32
   // stated): two block pairs in flight per wave with the activations
   // requested first, three for batched rows that request the weights first
   // (N = 17408, M = 8: 13.8 -> 12.5 us; at M = 1 three cost 5.28 -> 5.54);
-  // and at most two workgroups per compute unit up to four rows (M = 1:
-  // 5.28 -> 4.88 us, N = 5120 K = 17408: 12.1 -> 10.6; with the activations
-  // requested first, M = 4: 6.09 -> 5.11, N = 17408 M = 4: 12.4 -> 10.6),
-  // one beyond (eight rows of activations leave LDS for one).
+  // and up to two workgroups per compute unit where the LDS allows it (M = 1:
+  // 5.28 -> 4.88 us, N = 5120 K = 17408: 12.1 -> 10.6; M = 5: 6.58 -> 5.91,
+  // M = 7: 6.70 -> 6.16, with the activations requested first), except for
+  // five to eight rows of a matrix of 16 MB or more (one, in two subgroups).
   constexpr int kDepth = 3;  // weights first
-  constexpr int kMaxPerCu = MMAX <= 4 ? 2 : 1;
   const bool bounded = (uint64_t)N * (K >> 7) * kBlockBytes < (1ull << 32);  // buffer-load range
   const bool big = (uint64_t)N * (K >> 7) * kBlockBytes >= (16ull << 20);
+  const int kMaxPerCu = (MMAX <= 4 || !big) ? 2 : 1;
   // Five to eight rows of a matrix of 16 MB or more: two subgroups of 8 waves
   // per workgroup over one copy of the activations (measured on MI355X,
   // N = 17408, K = 5120: M = 8 12.45 -> 11.46 us, M = 5 12.54 -> 11.70; at
-  // N = K = 5120 one group stays faster, 6.74 against 7.31).
-  if constexpr (MMAX == 8) {
+  // N = K = 5120 one group stays faster, 6.74 against 7.31).  The 8-row
+  // instance serves the 6-row tier here too (the same bits; N = 17408,
+  // K = 5120, M = 6: 11.78 against 12.14 us for the 6-row instance).
+  if constexpr (MMAX > 4) {
     const size_t lds2 = pair_lds_bytes<8, 2>(M, K);
     if (big && lds2 <= kLdsMax && bounded) {
       const uint32_t pt = (M * (K >> 3) + 1023u) / 1024u;
@@ -767,11 +769,14 @@ hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32
     // set-up), or the first pairs' weights first.  Measured on MI355X
     // (interleaved A/B, graph-replayed): activations first for one row at any
     // size (N = 17408, K = 5120: 8.94 -> 8.48 us; N = 5120, K = 17408:
-    // 10.41 -> 9.95) and for 2..4 rows of a matrix under 16 MB (N = K = 5120,
-    // M = 2: 5.53 -> 4.86 us, M = 4: 6.68 -> 6.30); weights first for 5..8
-    // rows (even at M = 8) and for batched rows of larger matrices (N = 17408,
-    // M = 8: 12.5 against 13.7 us).
-    const bool wfirst = M > 4 || (M > 1 && big);
+    // 10.41 -> 9.95), for 2..4 rows of a matrix under 16 MB (N = K = 5120,
+    // M = 2: 5.53 -> 4.86 us, M = 4: 6.68 -> 6.30) and for 5..7 rows there
+    // when two workgroups share a compute unit; weights first for a lone
+    // workgroup per compute unit (N = K = 5120, M = 8: 6.62 against 6.70 us)
+    // and for batched rows of larger matrices (N = 17408, M = 8: 12.5 against
+    // 13.7 us).
+    const bool two_per_cu = kMaxPerCu >= 2 && 2u * lds <= kLdsMax;
+    const bool wfirst = M > 1 && (big || (M > 4 && !two_per_cu));
     // Staging chunks per thread: the smallest of 2, 3, 4, 5 and 10 that
     // covers A in one round (idle chunk slots cost loads and registers before
     // the staging barrier: N = K = 5120 M = 2: 4.86 -> 4.71 us, N = 5120
@@ -793,7 +798,7 @@ hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32
       }
     }
     if (!wfirst) {
-      if constexpr (MMAX <= 4) {
+      {
         if (per_thread <= 2) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 2, false>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
         if (per_thread <= 3) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 3, false>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
         if (per_thread <= 4) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 4, false>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
@@ -813,14 +818,19 @@ hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32
 
 }  // namespace
 
-bool q2_0_mfma_supports(uint32_t K, uint32_t m) { return K >= 1024u && ((K >> 7) % 8u) == 0 && m >= 1 && m <= 8; }
+bool q2_0_pairs_supports(uint32_t K) { return K >= 1024u && ((K >> 7) % 8u) == 0; }
 
-hipError_t launch_q2_0_mfma(const void *A, const void *B, void *C, uint32_t N, uint32_t K, uint32_t m,
-                            hipStream_t stream) {
-  if (m <= 1) return launch_mmax<1>(A, B, C, N, K, m, stream);
-  if (m <= 2) return launch_mmax<2>(A, B, C, N, K, m, stream);
-  if (m <= 4) return launch_mmax<4>(A, B, C, N, K, m, stream);
-  return launch_mmax<8>(A, B, C, N, K, m, stream);
+hipError_t launch_q2_0_pairs(const void *A, const void *B, void *C, uint32_t N, uint32_t K, uint32_t m,
+                             uint32_t width, hipStream_t stream) {
+  if (m == 0 || m > width) return hipErrorInvalidValue;
+  switch (width) {
+    case 1: return launch_mmax<1>(A, B, C, N, K, m, stream);
+    case 2: return launch_mmax<2>(A, B, C, N, K, m, stream);
+    case 4: return launch_mmax<4>(A, B, C, N, K, m, stream);
+    case 6: return launch_mmax<6>(A, B, C, N, K, m, stream);
+    case 8: return launch_mmax<8>(A, B, C, N, K, m, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace wqd

@@ -22,11 +22,12 @@ __device__ __forceinline__ void even_rows(uint32_t N, uint32_t b, uint32_t G, ui
 hipError_t launch_q2_0_valu(const void *A, const void *B, void *C, uint32_t N,
                             uint32_t K, uint32_t m, hipStream_t stream);
 
-// Same operation on the matrix-core kernel, for 1..16 rows.  Requires
-// q2_0_mfma_supports(K, m): K/128 a multiple of 8.
-bool q2_0_mfma_supports(uint32_t K, uint32_t m);
-hipError_t launch_q2_0_mfma(const void *A, const void *B, void *C, uint32_t N,
-                            uint32_t K, uint32_t m, hipStream_t stream);
+// Same operation on the matrix-core kernel, 1..8 rows per launch, for K a
+// multiple of 1024 (q2_0_pairs_supports).  `width` (1, 2, 4, 6 or 8, at
+// least m) picks the compiled row tier; every tier gives a row the same bits.
+bool q2_0_pairs_supports(uint32_t K);
+hipError_t launch_q2_0_pairs(const void *A, const void *B, void *C, uint32_t N,
+                             uint32_t K, uint32_t m, uint32_t width, hipStream_t stream);
 
 // Enqueue the W8A16 M16 GEMM for 1..16 rows; A and C row pitches lda / ldc
 // in elements; band = 0 (the weight rows split evenly over the workgroups) or

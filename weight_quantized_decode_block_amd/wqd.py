@@ -24,6 +24,7 @@ Q2_0_GROUP = 128
 Q2_0_BLOCK_BYTES = 34
 Q2_0_BATCHM_MAX_M = 8
 W8A16_MAX_M = 16
+Q2_0_TIER_WIDTHS = (1, 2, 4, 6, 8)  # WQD_Q2_0_TIER_WIDTHS, narrowest first
 
 _lib = None
 
@@ -60,6 +61,12 @@ def lib() -> ctypes.CDLL:
     L.q2_0_pack.restype = ctypes.c_int
     L.q2_0_batchm_chunks.argtypes = [u32, u32, u32, ctypes.POINTER(ctypes.c_uint64), u32]
     L.q2_0_batchm_chunks.restype = u32
+    L.q2_0_select_tier.argtypes = [u32, u32, ctypes.c_int]
+    L.q2_0_select_tier.restype = ctypes.c_int
+    L.q2_0_tier_width.argtypes = [u32]
+    L.q2_0_tier_width.restype = u32
+    L.q2_0_exact_m_tiers_enabled.argtypes = []
+    L.q2_0_exact_m_tiers_enabled.restype = ctypes.c_int
     L.wqd_last_error.argtypes = []
     L.wqd_last_error.restype = ctypes.c_char_p
     _lib = L
@@ -173,3 +180,18 @@ def q2_0_batchm_chunks(M: int, K: int, N: int) -> list[tuple[int, int, int]]:
     buf = (ctypes.c_uint64 * max(3 * count, 1))()
     L.q2_0_batchm_chunks(M, K, N, buf, count)
     return [(int(buf[3 * i]), int(buf[3 * i + 1]), int(buf[3 * i + 2])) for i in range(count)]
+
+
+def q2_0_select_tier(m: int, present_mask: int, exact_m: bool) -> int | None:
+    """Index into Q2_0_TIER_WIDTHS of the tier that serves m rows, or None."""
+    i = int(lib().q2_0_select_tier(m, present_mask, 1 if exact_m else 0))
+    return None if i < 0 else i
+
+
+def q2_0_tier_width(m: int) -> int:
+    """Row width the Q2_0 matrix-core kernel runs m rows on in this process (0: none)."""
+    return int(lib().q2_0_tier_width(m))
+
+
+def q2_0_exact_m_tiers_enabled() -> bool:
+    return bool(lib().q2_0_exact_m_tiers_enabled())
