@@ -215,13 +215,25 @@ def sweep_list():
 
 
 # ------------------------------------------------------------------- timing
+# Fewest launches in one captured graph: a graph of a small ring (8 copies of
+# a small matrix) replays faster than the host enqueues the next replay.
+MIN_GRAPH_STEPS = 64
+
+
+def graph_len(R: int) -> int:
+    """Steps in the full graph: the ring walked whole, as many times as needed
+    to reach MIN_GRAPH_STEPS (step i reads copy i mod R)."""
+    return R * max(1, math.ceil(MIN_GRAPH_STEPS / R))
+
+
 def timed_plan(R: int, steps: int):
     """How the timed region walks the ring of R weight copies: `full` replays
-    of a graph over copies 0..R-1, then one graph over copies 0..rest-1
-    (steps = full * R + rest, exactly).  An untimed replay of the full-ring
-    graph runs just before, so every timed step reads the copy that was last
-    read R steps earlier: R - 1 other copies in between."""
-    full, rest = divmod(steps, R)
+    of a graph over steps 0..L-1 (L = graph_len(R), step i on copy i mod R),
+    then one graph over steps 0..rest-1 (steps = full * L + rest, exactly).
+    An untimed replay of the full graph runs just before, so every timed step
+    reads the copy that was last read R steps earlier: R - 1 other copies in
+    between."""
+    full, rest = divmod(steps, graph_len(R))
     return full, rest
 
 
@@ -296,9 +308,9 @@ def time_workload(torch, wqd, wl, steps, warmup):
     eager = t0.elapsed_time(t1) / steps
 
     full, rest = timed_plan(R, steps)
-    g_full = _capture(torch, wqd, wl, range(R))
+    g_full = _capture(torch, wqd, wl, range(graph_len(R)))
     g_rest = _capture(torch, wqd, wl, range(rest)) if rest else None
-    g_full.replay()  # untimed: the whole ring once, ending at copy R - 1
+    g_full.replay()  # untimed: the whole ring, ending at copy R - 1
     _gpu_pre_delay(torch)
     t0.record(stream)
     for _ in range(full):

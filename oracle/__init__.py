@@ -10,7 +10,8 @@ Pages followed (cited by title and section):
   * "gemv_q2_vec.rs", module doc and ``mod tests`` helper ``gemv_row``:
     the Q2_0 per-row reference (fp32, ascending k, BF16 store).
   * "w8a16_gemm_m16.rs", module doc: FP8 E4M3 weights with FP32 128x128 block
-    scales folded once per 128-K block onto an fp32 outer accumulator.
+    scales; each 128-K block's fp32 sum is scaled once and added to an fp32
+    total per output.
 """
 from __future__ import annotations
 

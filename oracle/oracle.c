@@ -20,10 +20,10 @@
  *         w = ((code & 3) - 1) * d and d round-tripped through fp16, and the
  *         result stored as BF16 (round to nearest even).
  *   [W8]  "w8a16_gemm_m16.rs" (metrale_model_layers layers/ops), module doc
- *         and the doc of w8a16_gemm_m16: FP8 E4M3 weights [N,K], FP32 block
- *         scales [N/128, K/128], the 128-K block scale folded once per block
- *         onto an FP32 outer accumulator, never per element and never into
- *         BF16; BF16 input and output.
+ *         and the doc of w8a16_gemm_m16: FP8 E4M3 weights [N,K], FP32 scales
+ *         [N/128, K/128]; per output, each 128-K block's fp32 sum times the
+ *         block's scale is added to an fp32 total (one scaling per block, no
+ *         BF16 in between); BF16 input and output.
  *
  * Readings where the pages are silent (each is listed in the design notes):
  *   - block_q2_0 byte layout: fp16 d little-endian in bytes 0-1, then 32

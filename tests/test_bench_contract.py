@@ -47,9 +47,11 @@ def test_weight_rings_exceed_the_on_die_cache():
 def test_timed_plan_times_exactly_the_requested_steps():
     b = _bench()
     for R in (8, 21, 23, 78):
+        L = b.graph_len(R)
+        assert L % R == 0 and L >= b.MIN_GRAPH_STEPS and L - R < b.MIN_GRAPH_STEPS
         for steps in (1, 5, 20, 200, 997, 1000, 2000):
             full, rest = b.timed_plan(R, steps)
-            assert full * R + rest == steps and 0 <= rest < R
+            assert full * L + rest == steps and 0 <= rest < L
 
 
 def test_every_timed_read_is_cold_at_the_drivers_step_count():

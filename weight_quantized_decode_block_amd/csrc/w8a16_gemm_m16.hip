@@ -2,10 +2,11 @@
 //
 //   C[m,n] = bf16( sum_b S[n/128][b] * sum_{k in block b} A[m,k] * W[n,k] ),  m < M <= 16
 //
-// Operation: page "w8a16_gemm_m16.rs", module doc (FP8 E4M3 weights [N,K],
-// FP32 block scales [N/128, K/128] folded once per 128-K block onto an fp32
-// outer accumulator, never per element and never into BF16; the M tile is the
-// matrix instruction's 16 rows) and the doc of w8a16_gemm_m16 (BF16 A [m,k],
+// Operation: page "w8a16_gemm_m16.rs", module doc (FP8 E4M3 weights [N,K]
+// with FP32 scales [N/128, K/128]: each 128-K block's fp32 sum is multiplied
+// by its scale once and added to the output's fp32 total, with no scaling of
+// single products and no BF16 intermediate; the M tile is the matrix
+// instruction's 16 rows) and the doc of w8a16_gemm_m16 (BF16 A [m,k],
 // BF16 C [m,n], rows >= m untouched).  The pages' Hopper design (mma.sync
 // m16n8k16, 32 columns and 128 threads per CTA, A staged with cp.async) is
 // not used; this kernel is laid out for gfx950 as follows.

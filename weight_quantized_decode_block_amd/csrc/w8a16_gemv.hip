@@ -4,13 +4,14 @@
 //   C[m,n] = bf16( sum_b S[n/128][b] * inner(m, n, b) ),
 //   inner(m, n, b) = fp32 sum of A[m,k] * W[n,k] over the 128 k of block b
 //
-// Operation: page "w8a16_gemm_m16.rs", module doc: besides the matrix-core
-// kernel there is a scalar W8A16 GEMV (w8a16_gemv_batch16) that spends one
-// multiply-add per weight byte and activation row on the ordinary ALUs, and
-// whose results the matrix-core kernel does not reproduce bit for bit; the
-// 128-K block scale is folded once per block onto an fp32 outer accumulator,
-// never per element and never into BF16.  This is that scalar path, laid out
-// for gfx950; it keeps its own fixed order (below), the same for every M.
+// Operation: page "w8a16_gemm_m16.rs", module doc.  Beside its matrix-core
+// kernel the page keeps a scalar GEMV (w8a16_gemv_batch16): one multiply-add
+// per weight and activation row on the general-purpose ALUs, with bits that
+// need not equal the matrix-core kernel's.  Scales as there: a block's 128
+// products are summed in fp32, that sum is multiplied by the block's scale
+// and the product added to the output's fp32 total; BF16 appears only at the
+// store.  This is that scalar path, laid out for gfx950; it keeps its own
+// fixed order (below), the same for every M.
 //
 // Work layout
 //   * One workgroup of 8 waves per CU owns an even share [r0, r1) of the N
