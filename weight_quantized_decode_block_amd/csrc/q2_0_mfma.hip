@@ -52,6 +52,8 @@
 // activation row m always sits in MFMA rows m and 8 + m.  So M=1 and every
 // batched M give the same bits.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 #include <stdint.h>
 
 #include "wqd_internal.h"
@@ -595,12 +597,12 @@ __global__ __launch_bounds__(64 * NW * SG) void q2_0_pairs_kernel(const uint16_t
     for (int rr = 0; rr < NF; ++rr) sum[rr] = __builtin_fmaf((float)d, x[rr], sum[rr]);
   };
 
-  // One unit: compute from its ring registers, then request the unit DEPTH
-  // ahead into the same registers (reusing them in place keeps the ring free
-  // of register copies, which would wait for loads still in flight), and
+  // One unit: compute from its ring registers, then (LD) request the unit
+  // DEPTH ahead into the same registers (reusing them in place keeps the ring
+  // free of register copies, which would wait for loads still in flight), and
   // after the wave's last pair of the tile add the tile's partial sums.
   Cursor cc = {0u, 0u, 0u, first_row()};
-  auto step = [&](PairRegs &r) {
+  auto step = [&](PairRegs &r, auto ld_next) {
     const uint32_t j = cc.j, u = cc.u, row = cc.row;
     const uint32_t p = wave + NW * u;
     const bool own = SG == 1 || j < own_tiles;
@@ -610,7 +612,7 @@ __global__ __launch_bounds__(64 * NW * SG) void q2_0_pairs_kernel(const uint16_t
       else
         unit(r, p, j == 0u, acc[NACC - 1]);
     }
-    r = issue_next();
+    if constexpr (decltype(ld_next)::value) r = issue_next();
     advance(cc);
     if (u + 1u == upw) {  // tile done: add the 16 partial sums of each output in fixed order
       const uint32_t par = j & 1u;
@@ -642,13 +644,57 @@ __global__ __launch_bounds__(64 * NW * SG) void q2_0_pairs_kernel(const uint16_t
     }
   };
 
-  while (cc.q + DEPTH <= nq) {
+  // Batched rows with a ring of two request only units the wave computes:
+  // the loop runs while all of its requests are, and the 2 or 3 units left
+  // after it run as straight-line code with exactly the requests still needed
+  // (a request past the wave's last unit occupies the compute unit's address
+  // path; one behind a branch makes the compiler wait for every load in
+  // flight where the branch rejoins).  Measured on MI355X against requests
+  // past the end (interleaved A/B): N = K = 5120 M = 2 4.63 -> 4.52 us, M = 4
+  // 5.00 -> 4.86.  One row keeps the requests past the end (N = K = 5120:
+  // 4.47 against 4.48-4.52 drained, though N = K = 2048 drops 2.68 -> 2.59),
+  // and so does a ring of three (five to eight rows, weights first: M = 8 6.59
+  // against 6.77 us drained).
+  const std::true_type LD;
+  const std::false_type NOLD;
+  if constexpr (DEPTH != 2 || MMAX == 1) {
+    while (cc.q + DEPTH <= nq) {
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d) step(ring[d]);
+      for (int d = 0; d < DEPTH; ++d) step(ring[d], LD);
+    }
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d)
+      if (cc.q < nq) step(ring[d], LD);
+    return;
   }
+  while (cc.q + 2u * DEPTH <= nq) {
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d)
-    if (cc.q < nq) step(ring[d]);
+    for (int d = 0; d < DEPTH; ++d) step(ring[d], LD);
+  }
+  const uint32_t rem = nq - cc.q;
+  auto drain = [&](auto E) {  // E of the DEPTH ring units still request one more
+    constexpr int e = decltype(E)::value;
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      if (d < e)
+        step(ring[d], LD);
+      else
+        step(ring[d], NOLD);
+    }
+#pragma unroll
+    for (int d = 0; d < e; ++d) step(ring[d], NOLD);
+  };
+  if (rem >= (uint32_t)DEPTH) {
+    const uint32_t e = rem - DEPTH;  // < DEPTH
+    if (e == 0u)
+      drain(std::integral_constant<int, 0>{});
+    else
+      drain(std::integral_constant<int, 1>{});
+  } else {  // fewer units than the ring (the prologue requested a few past the end)
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d)
+      if ((uint32_t)d < rem) step(ring[d], NOLD);
+  }
 }
 
 // Launches KERN as a persistent grid: as many workgroups as fit on the device
