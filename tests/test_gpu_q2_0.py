@@ -248,3 +248,25 @@ def test_exact_row_tiers_equal_base_tier_bits(tmp_path):
         codes, d = gen.q2_0_weights(53, N, K, N + M)
         got = q2_0_gpu(A, wqd.q2_0_pack(codes, d), N, K)
         assert np.array_equal(got, base[key]), key
+
+
+@pytest.mark.parametrize("N,K,M", [(8, 1024, 2), (24, 1024, 3), (40, 2048, 4), (5000, 3072, 2), (300, 4096, 6),
+                                   (1000, 5120, 3), (4104, 6144, 5)])
+def test_two_deep_ring_drain_unit_counts(oracle_mod, N, K, M):
+    """Batched rows on a two-deep ring finish with straight-line code sized to
+    the units left: fewer units per wave than the ring (K = 1024: four pairs
+    for eight waves, so each wave has one unit per tile or an empty one), two
+    or three left after the loop (K = 2048 .. 6144 give 1 to 3 pairs per wave
+    and tile, over one to several tiles per workgroup).  Every row equals its
+    own M=1 launch, a canary row past M stays untouched and the outputs (or a
+    column sample holding the last one) are within tolerance of the oracle."""
+    print(f"drain N={N} K={K} M={M}", flush=True)
+    A, codes, d, packed = _case(59, N, K, M, salt=N * 5 + K + M)
+    Bd = dev_u8(packed)
+    got = q2_0_gpu(A, Bd, N, K, extra_rows=1)
+    assert np.all(got[M] == CANARY)
+    got = got[:M]
+    for m in range(M):
+        assert np.array_equal(got[m:m + 1], q2_0_gpu(A[m:m + 1], Bd, N, K, single=True)), m
+    cols = np.arange(N) if N <= 400 else np.union1d(gen.rng(959, N, K).choice(N, 256, replace=False), [N - 1])
+    check_parity(got[:, cols], oracle_mod.q2_0_gemv(A, codes[cols], d[cols]), f"q2_0 {N}x{K} M={M}")

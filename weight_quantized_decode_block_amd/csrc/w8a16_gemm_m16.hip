@@ -291,10 +291,15 @@ struct UnitRegs {
   float s;         // the block's scale
 };
 
+// Scale floats the units kernel can hold in LDS: the scale rows covering a
+// workgroup's weight rows.
+constexpr uint32_t kUnitScales = 512;
+
 template <int MMAX>
 struct UnitLayout {
   static constexpr int kPart = 0;  // [tile parity][wave][m][16] floats
-  static constexpr int kA = kPart + 2 * kWaves * MMAX * 16 * 4;
+  static constexpr int kS = kPart + 2 * kWaves * MMAX * 16 * 4;  // [scale row - g0][block] floats
+  static constexpr int kA = kS + (int)kUnitScales * 4;
 };
 
 template <int MMAX>
@@ -302,7 +307,7 @@ constexpr size_t unit_lds_bytes(uint32_t M, uint32_t K) {
   return (size_t)UnitLayout<MMAX>::kA + (size_t)M * (2u * K + 16u);
 }
 
-template <int MMAX, int DEPTH, int UA>
+template <int MMAX, int DEPTH, int UA, bool SL>
 __global__ __launch_bounds__(kThreads) void w8a16_units_kernel(const uint16_t *__restrict__ A,
                                                                const uint8_t *__restrict__ W,
                                                                const float *__restrict__ S,
@@ -354,6 +359,15 @@ __global__ __launch_bounds__(kThreads) void w8a16_units_kernel(const uint16_t *_
     r1 = min(r0 + 16u * band, N);
   }
   const uint32_t my_tiles = (r1 - r0 + 15u) >> 4;
+  // SL: the scale rows of rows [r0, r1), at most kUnitScales floats (the
+  // launcher checks), requested now and kept in LDS for the whole launch, so
+  // the weight requests carry no 4-byte scale requests beside them
+  const uint32_t g0 = r0 >> 7;
+  const uint32_t nsc = SL ? (((r1 - 1u) >> 7) - g0 + 1u) * nb : 0u;
+  float sv = 0.0f;
+  if constexpr (SL) {
+    if (tid < nsc) sv = S[g0 * nb + tid];
+  }
   // blocks of a tile owned by this wave: wave, wave + 8, ...; a wave that
   // owns none (K < 1024) runs one empty unit per tile to meet the barrier
   const uint32_t upw = nb > wave ? (nb - wave + kWaves - 1) / kWaves : 1u;
@@ -391,9 +405,13 @@ __global__ __launch_bounds__(kThreads) void w8a16_units_kernel(const uint16_t *_
     UnitRegs r;
     r.w0 = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, voff, soff, 0);
     r.w1 = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, voff + 16u, soff, 0);
-    // the scale of this lane's own row: a tile need not sit inside one 128-row scale group
-    const uint32_t srow = (row < r1 ? row : r1 - 1u) >> 7;
-    r.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srsrc, live ? srow * nb * 4u : kPastEnd, 4u * b, 0));
+    if constexpr (SL) {
+      r.s = 0.0f;
+    } else {
+      // the scale of this lane's own row: a tile need not sit inside one 128-row scale group
+      const uint32_t srow = (row < r1 ? row : r1 - 1u) >> 7;
+      r.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srsrc, live ? srow * nb * 4u : kPastEnd, 4u * b, 0));
+    }
     advance(ld);
     return r;
   };
@@ -410,6 +428,9 @@ __global__ __launch_bounds__(kThreads) void w8a16_units_kernel(const uint16_t *_
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) ring[d] = issue_next();
     a_store();
+    if constexpr (SL) {
+      if (tid < nsc) reinterpret_cast<float *>(lds + L::kS)[tid] = sv;
+    }
     for (uint32_t base = UA * kThreads; base < total; base += UA * kThreads) {
       a_load(base);
       a_store();
@@ -418,7 +439,13 @@ __global__ __launch_bounds__(kThreads) void w8a16_units_kernel(const uint16_t *_
   }
 
   f32x4_t outer = {0.0f, 0.0f, 0.0f, 0.0f};
-  auto unit = [&](const UnitRegs &r, uint32_t b) {
+  auto unit = [&](const UnitRegs &r, uint32_t b, uint32_t n0) {
+    float sc = r.s;
+    if constexpr (SL) {  // this lane's row's scale, from LDS
+      const uint32_t row = n0 + i;
+      const uint32_t srow = (row < r1 ? row : r1 - 1u) >> 7;
+      sc = reinterpret_cast<const float *>(lds + L::kS)[(srow - g0) * nb + b];
+    }
     const uint8_t *act = lds + L::kA + a_lane + 256u * b;
     bf16x8_t a[4];
 #pragma unroll
@@ -429,14 +456,14 @@ __global__ __launch_bounds__(kThreads) void w8a16_units_kernel(const uint16_t *_
     x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2], weights8(r.w1.x, r.w1.y), x, 0, 0, 0);
     x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[3], weights8(r.w1.z, r.w1.w), x, 0, 0, 0);
 #pragma unroll
-    for (int rr = 0; rr < NF; ++rr) outer[rr] = __fadd_rn(outer[rr], __fmul_rn(r.s, x[rr]));
+    for (int rr = 0; rr < NF; ++rr) outer[rr] = __fadd_rn(outer[rr], __fmul_rn(sc, x[rr]));
   };
 
   Cursor cc = {0u, 0u, 0u, r0};
   auto step = [&](UnitRegs &r) {
     const uint32_t j = cc.j, u = cc.u, n0 = cc.n0;
     const uint32_t b = wave + kWaves * u;
-    if (b < nb) unit(r, b);
+    if (b < nb) unit(r, b, n0);
     r = issue_next();
     advance(cc);
     if (u + 1u == upw) {  // tile done: add the 8 waves' partial tiles in wave order
@@ -507,6 +534,20 @@ hipError_t launch_units(size_t lds, uint32_t ntiles, uint32_t band, hipStream_t 
   return hipGetLastError();
 }
 
+template <int MMAX, bool SL>
+hipError_t launch_units_sl(uint32_t per_thread, size_t lds, uint32_t ntiles, uint32_t band, hipStream_t stream,
+                           const uint16_t *a, const uint8_t *w, const float *S, uint16_t *c, uint32_t M, uint32_t N,
+                           uint32_t K, uint32_t lda, uint32_t ldc) {
+  // staging chunks per thread: the smallest of 2, 3, 4, 5 and 10 covering A in
+  // one round (measured on MI355X: N = K = 5120 M = 4: 8.71 -> 8.42 us;
+  // N = 5120 K = 17408 M = 1: 20.5 -> 20.1)
+  if (per_thread <= 2) return launch_units<w8a16_units_kernel<MMAX, 4, 2, SL>>(lds, ntiles, band, stream, a, w, S, c, M, N, K, lda, ldc);
+  if (per_thread <= 3) return launch_units<w8a16_units_kernel<MMAX, 4, 3, SL>>(lds, ntiles, band, stream, a, w, S, c, M, N, K, lda, ldc);
+  if (per_thread <= 4) return launch_units<w8a16_units_kernel<MMAX, 4, 4, SL>>(lds, ntiles, band, stream, a, w, S, c, M, N, K, lda, ldc);
+  if (per_thread <= 5) return launch_units<w8a16_units_kernel<MMAX, 4, 5, SL>>(lds, ntiles, band, stream, a, w, S, c, M, N, K, lda, ldc);
+  return launch_units<w8a16_units_kernel<MMAX, 4, 10, SL>>(lds, ntiles, band, stream, a, w, S, c, M, N, K, lda, ldc);
+}
+
 template <int MMAX>
 hipError_t launch_units_mmax(const void *A, const void *W, const float *S, void *C, uint32_t M, uint32_t N,
                              uint32_t K, uint32_t lda, uint32_t ldc, uint32_t band, hipStream_t stream) {
@@ -516,14 +557,23 @@ hipError_t launch_units_mmax(const void *A, const void *W, const float *S, void 
   const auto *w = static_cast<const uint8_t *>(W);
   auto *c = static_cast<uint16_t *>(C);
   const uint32_t per_thread = (M * (K >> 3) + kThreads - 1) / kThreads;
-  // staging chunks per thread: the smallest of 2, 3, 4, 5 and 10 covering A in
-  // one round (measured on MI355X: N = K = 5120 M = 4: 8.71 -> 8.42 us;
-  // N = 5120 K = 17408 M = 1: 20.5 -> 20.1)
-  if (per_thread <= 2) return launch_units<w8a16_units_kernel<MMAX, 4, 2>>(lds, ntiles, band, stream, a, w, S, c, M, N, K, lda, ldc);
-  if (per_thread <= 3) return launch_units<w8a16_units_kernel<MMAX, 4, 3>>(lds, ntiles, band, stream, a, w, S, c, M, N, K, lda, ldc);
-  if (per_thread <= 4) return launch_units<w8a16_units_kernel<MMAX, 4, 4>>(lds, ntiles, band, stream, a, w, S, c, M, N, K, lda, ldc);
-  if (per_thread <= 5) return launch_units<w8a16_units_kernel<MMAX, 4, 5>>(lds, ntiles, band, stream, a, w, S, c, M, N, K, lda, ldc);
-  return launch_units<w8a16_units_kernel<MMAX, 4, 10>>(lds, ntiles, band, stream, a, w, S, c, M, N, K, lda, ldc);
+  // Scale rows in LDS when those of every workgroup's rows fit: a range of R
+  // rows touches at most (R + 126) / 128 + 1 scale rows, and a workgroup holds
+  // at most ceil(N / CUs) rows (one per CU, fewer when there are fewer tiles)
+  // or 16 * band.
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    cus = n > 0 ? n : 1;
+  }
+  const uint32_t wgs = band > 0u ? (ntiles + band - 1u) / band : (ntiles < (uint32_t)cus ? ntiles : (uint32_t)cus);
+  const uint32_t rows_max = band > 0u ? 16u * band : (N + wgs - 1u) / wgs;
+  const uint64_t scales = (uint64_t)((rows_max + 126u) / 128u + 1u) * (K >> 7);
+  if (scales <= kUnitScales) return launch_units_sl<MMAX, true>(per_thread, lds, ntiles, band, stream, a, w, S, c, M, N, K, lda, ldc);
+  return launch_units_sl<MMAX, false>(per_thread, lds, ntiles, band, stream, a, w, S, c, M, N, K, lda, ldc);
 }
 
 // ---------------------------------------------------------------------------
