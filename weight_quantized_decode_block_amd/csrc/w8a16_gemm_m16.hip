@@ -599,7 +599,7 @@ hipError_t launch_units_mmax(const void *A, const void *W, const float *S, void 
 //     every tile); past the last tile the requests use an offset beyond the
 //     buffer, which fetches nothing.
 // ---------------------------------------------------------------------------
-template <int NBW, bool SL>
+template <int NBW>
 __global__ __launch_bounds__(kThreads) void w8a16_regs_kernel(const uint16_t *__restrict__ A,
                                                               const uint8_t *__restrict__ W,
                                                               const float *__restrict__ S,
@@ -614,21 +614,6 @@ __global__ __launch_bounds__(kThreads) void w8a16_regs_kernel(const uint16_t *__
   const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t i = lane & 15u, g = lane >> 4;
   const uint32_t nb = K >> 7;
-  uint32_t r0, r1;  // rows of this workgroup, as in the kernel above
-  if (band == 0u) {
-    even_rows(N, blockIdx.x, gridDim.x, r0, r1);
-  } else {
-    r0 = blockIdx.x * 16u * band;
-    r1 = min(r0 + 16u * band, N);
-  }
-  // SL: the scale rows of rows [r0, r1) in LDS (as in the kernel above),
-  // requested first so that storing them waits for nothing else
-  const uint32_t g0 = r0 >> 7;
-  const uint32_t nsc = SL ? (((r1 - 1u) >> 7) - g0 + 1u) * nb : 0u;
-  float sv = 0.0f;
-  if constexpr (SL) {
-    if (tid < nsc) sv = S[g0 * nb + tid];
-  }
   // the activations of the wave's blocks, requested before any other set-up
   bf16x8_t a[NBW][4];
   {
@@ -639,6 +624,13 @@ __global__ __launch_bounds__(kThreads) void w8a16_regs_kernel(const uint16_t *__
 #pragma unroll
       for (int j = 0; j < 4; ++j) a[u][j] = *reinterpret_cast<const bf16x8_t *>(arow + 128u * b + 8u * j);
     });
+  }
+  uint32_t r0, r1;  // rows of this workgroup, as in the kernel above
+  if (band == 0u) {
+    even_rows(N, blockIdx.x, gridDim.x, r0, r1);
+  } else {
+    r0 = blockIdx.x * 16u * band;
+    r1 = min(r0 + 16u * band, N);
   }
   const uint32_t ntile = (r1 - r0 + 15u) >> 4;
   const uint32_t upw = nb > wave ? (nb - wave + kWaves - 1u) / kWaves : 0u;  // <= NBW
@@ -657,12 +649,8 @@ __global__ __launch_bounds__(kThreads) void w8a16_regs_kernel(const uint16_t *__
     UnitRegs r;
     r.w0 = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, voff, 128u * b, 0);
     r.w1 = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, voff + 16u, 128u * b, 0);
-    if constexpr (SL) {
-      r.s = 0.0f;
-    } else {
-      r.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srsrc, ok ? srow * nb * 4u : kPastEnd,
-                                                                           4u * b, 0));
-    }
+    r.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srsrc, ok ? srow * nb * 4u : kPastEnd,
+                                                                         4u * b, 0));
     return r;
   };
 
@@ -673,11 +661,6 @@ __global__ __launch_bounds__(kThreads) void w8a16_regs_kernel(const uint16_t *__
       ring[u] = issue(0u, (uint32_t)u);
     });
   }
-  const float *sl = reinterpret_cast<const float *>(lds + L::kS);
-  if constexpr (SL) {
-    if (tid < nsc) reinterpret_cast<float *>(lds + L::kS)[tid] = sv;
-    __syncthreads();
-  }
 
   float *part = reinterpret_cast<float *>(lds + L::kPart);
   for (uint32_t t = 0; t < ntile; ++t) {
@@ -687,19 +670,13 @@ __global__ __launch_bounds__(kThreads) void w8a16_regs_kernel(const uint16_t *__
       if ((uint32_t)u < upw) {
         const UnitRegs r = ring[u];
         ring[u] = issue(t + 1u, (uint32_t)u);
-        float sc = r.s;
-        if constexpr (SL) {  // this lane's row's scale, from LDS
-          const uint32_t b = wave + kWaves * (uint32_t)u;
-          const uint32_t row = r0 + 16u * t + i;
-          sc = sl[(((row < r1 ? row : r1 - 1u) >> 7) - g0) * nb + b];
-        }
         f32x4_t x = {0.0f, 0.0f, 0.0f, 0.0f};
         x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][0], weights8(r.w0.x, r.w0.y), x, 0, 0, 0);
         x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][1], weights8(r.w0.z, r.w0.w), x, 0, 0, 0);
         x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][2], weights8(r.w1.x, r.w1.y), x, 0, 0, 0);
         x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][3], weights8(r.w1.z, r.w1.w), x, 0, 0, 0);
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) outer[rr] = __fadd_rn(outer[rr], __fmul_rn(sc, x[rr]));
+        for (int rr = 0; rr < 4; ++rr) outer[rr] = __fadd_rn(outer[rr], __fmul_rn(r.s, x[rr]));
       }
     });
     // the 8 waves' partial tiles, added in wave order (tile parity alternates
@@ -727,12 +704,12 @@ __global__ __launch_bounds__(kThreads) void w8a16_regs_kernel(const uint16_t *__
 template <int NBW>
 hipError_t launch_regs(const void *A, const void *W, const float *S, void *C, uint32_t M, uint32_t N, uint32_t K,
                        uint32_t lda, uint32_t ldc, uint32_t band, hipStream_t stream) {
-  // scales per block from memory: staging them in LDS first (as the kernel
-  // above does) measured mixed here, N = K = 5120 M = 16 11.77 -> 11.60 us but
-  // N = 17408 M = 16 24.31 -> 24.88 (the staging barrier holds the first tile)
-  return launch_units<w8a16_regs_kernel<NBW, false>>((size_t)UnitLayout<16>::kA, (N + 15u) / 16u, band, stream,
-                                                     static_cast<const uint16_t *>(A), static_cast<const uint8_t *>(W),
-                                                     S, static_cast<uint16_t *>(C), M, N, K, lda, ldc);
+  // Scales per block from memory.  Staging them in LDS first, as the kernel
+  // above does, measured mixed here (N = K = 5120 M = 16 11.77 -> 11.60 us,
+  // N = 17408 M = 16 24.31 -> 24.88: the staging barrier holds the first tile).
+  return launch_units<w8a16_regs_kernel<NBW>>((size_t)UnitLayout<16>::kA, (N + 15u) / 16u, band, stream,
+                                              static_cast<const uint16_t *>(A), static_cast<const uint8_t *>(W), S,
+                                              static_cast<uint16_t *>(C), M, N, K, lda, ldc);
 }
 
 // ---------------------------------------------------------------------------
