@@ -389,13 +389,11 @@ constexpr size_t pair_lds_bytes(uint32_t M, uint32_t K) {
 }
 
 // One block pair's bytes for this lane: the aligned 3-dword window holding
-// its 8 code bytes and, with SEPD, the dword holding its fp16 scale (low
-// half).  Without SEPD the scale comes from the window of lane g = 0 of the
-// same column, which starts at the half's scale (first block) or two bytes
-// before it (second block), through one cross-lane permute.
+// its 8 code bytes.  The fp16 scale comes from the window of lane g = 0 of
+// the same column, which starts at the half's scale (first block) or two
+// bytes before it (second block), through one cross-lane permute.
 struct PairRegs {
   u32x3_t w;
-  uint32_t d;
 };
 
 // NW waves per workgroup (4 or 8).  Pair p of a tile belongs to accumulation
@@ -403,8 +401,8 @@ struct PairRegs {
 // accumulator per slot it owns, so the sums are those of the per-phase kernel.
 // Weight bytes go straight from memory to the lanes that use them (buffer
 // loads bounded by the matrix size): lane (h, r, g) reads 12 bytes at
-// 68p + 32h + 8g of weight row r and, with SEPD, 2 bytes (the scale) at
-// 68p + 34h; without SEPD the scale is taken from lane (h, r, 0)'s 12 bytes.
+// 68p + 32h + 8g of weight row r; the scale is taken from lane (h, r, 0)'s 12
+// bytes.
 //
 // SG = 2 runs two such groups of NW waves in one workgroup over one LDS copy
 // of the activations: subgroup s walks the tiles of virtual workgroup
@@ -413,7 +411,18 @@ struct PairRegs {
 // barrier is shared, so both subgroups walk as many tiles as subgroup 0; the
 // tiles past subgroup 1's own count load in bounds (the last tile) and
 // neither compute nor store.
-template <int MMAX, int NW, int DEPTH, int UA, bool WFIRST, int SG = 1, bool SEPD = false>
+// f(integral_constant<e>) for the runtime value e in [E, D)
+template <int E, int D, typename F>
+__device__ __forceinline__ void drain_case(uint32_t e, F &&f) {
+  if constexpr (E < D) {
+    if (e == (uint32_t)E)
+      f(std::integral_constant<int, E>{});
+    else
+      drain_case<E + 1, D>(e, f);
+  }
+}
+
+template <int MMAX, int NW, int DEPTH, int UA, bool WFIRST, int SG = 1, int LATE = 0, bool DRN = false>
 __global__ __launch_bounds__(64 * NW * SG) void q2_0_pairs_kernel(const uint16_t *__restrict__ A,
                                                                   const uint8_t *__restrict__ B,
                                                                   uint16_t *__restrict__ C, uint32_t N, uint32_t K,
@@ -487,7 +496,6 @@ __global__ __launch_bounds__(64 * NW * SG) void q2_0_pairs_kernel(const uint16_t
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(B), (short)0, (int)(N * rb), 0x00020000);
   const uint32_t row_off = min(rw, N - 1u) * rb;  // rows past N (N < 8) re-read row N - 1
   const uint32_t w_voff = row_off + 32u * h + 8u * g;
-  const uint32_t d_voff = row_off + 34u * h;  // used with SEPD
   // Unit q of this wave is pair wave + NW*u of tile j (q = j * upw + u).
   // Two wave-uniform cursors walk the units in order, one for the loads
   // (DEPTH units ahead) and one for the compute, so the per-unit bookkeeping
@@ -514,11 +522,6 @@ __global__ __launch_bounds__(64 * NW * SG) void q2_0_pairs_kernel(const uint16_t
     const uint32_t soff = ld.q < nq ? ld.row * rb + 68u * p : soff_first;
     PairRegs r;
     r.w = __builtin_amdgcn_raw_buffer_load_b96(wrsrc, w_voff, soff, 0);
-    if constexpr (SEPD) {
-      r.d = __builtin_amdgcn_raw_buffer_load_b16(wrsrc, d_voff, soff, 0);
-    } else {
-      r.d = 0u;
-    }
     advance(ld);
     return r;
   };
@@ -546,7 +549,7 @@ __global__ __launch_bounds__(64 * NW * SG) void q2_0_pairs_kernel(const uint16_t
     // rows of a small matrix, where the activation copy is on
     // the critical path)
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d) ring[d] = issue_next();
+    for (int d = 0; d < DEPTH - LATE; ++d) ring[d] = issue_next();
     if constexpr (WFIRST) {
       a_load(0u);
     } else {
@@ -558,6 +561,10 @@ __global__ __launch_bounds__(64 * NW * SG) void q2_0_pairs_kernel(const uint16_t
       a_store();
     }
     __syncthreads();
+    // LATE ring slots are requested only now, so that their requests do not
+    // queue ahead of the activation copy
+#pragma unroll
+    for (int d = DEPTH - LATE; d < DEPTH; ++d) ring[d] = issue_next();
   }
 
   f32x4_t acc[NACC];
@@ -580,11 +587,8 @@ __global__ __launch_bounds__(64 * NW * SG) void q2_0_pairs_kernel(const uint16_t
     }
     const uint32_t w0 = __builtin_amdgcn_perm(r.w.y, r.w.x, sel);
     const uint32_t w1 = __builtin_amdgcn_perm(r.w.z, r.w.y, sel);
-    uint32_t dbits = r.d;
-    if constexpr (!SEPD) {
-      const uint32_t own_d = h ? (r.w.x >> 16) : (r.w.x & 0xFFFFu);  // meaningful on lanes g = 0
-      dbits = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(i << 2), (int)own_d);
-    }
+    const uint32_t own_d = h ? (r.w.x >> 16) : (r.w.x & 0xFFFFu);  // meaningful on lanes g = 0
+    const uint32_t dbits = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(i << 2), (int)own_d);
     const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)dbits);
     bf16x8_t b0, b1, b2, b3;
     decode_word(w0, b0, b1);
@@ -644,20 +648,18 @@ __global__ __launch_bounds__(64 * NW * SG) void q2_0_pairs_kernel(const uint16_t
     }
   };
 
-  // Batched rows with a ring of two request only units the wave computes:
-  // the loop runs while all of its requests are, and the 2 or 3 units left
-  // after it run as straight-line code with exactly the requests still needed
-  // (a request past the wave's last unit occupies the compute unit's address
+  // DRN: only units the wave computes are requested.  The loop runs while
+  // all of its requests are, and the DEPTH..2 DEPTH - 1 units left after it
+  // run as straight-line code with exactly the requests still needed (a
+  // request past the wave's last unit occupies the compute unit's address
   // path; one behind a branch makes the compiler wait for every load in
-  // flight where the branch rejoins).  Measured on MI355X against requests
-  // past the end (interleaved A/B): N = K = 5120 M = 2 4.63 -> 4.52 us, M = 4
-  // 5.00 -> 4.86.  One row keeps the requests past the end (N = K = 5120:
-  // 4.47 against 4.48-4.52 drained, though N = K = 2048 drops 2.68 -> 2.59),
-  // and so does a ring of three (five to eight rows, weights first: M = 8 6.59
+  // flight where the branch rejoins).  Without DRN the ring requests units
+  // past the end (re-reading the wave's first pair), which measured better
+  // for the three-deep weights-first ring of five to eight rows (M = 8: 6.59
   // against 6.77 us drained).
   const std::true_type LD;
   const std::false_type NOLD;
-  if constexpr (DEPTH != 2 || MMAX == 1) {
+  if constexpr (!DRN) {
     while (cc.q + DEPTH <= nq) {
 #pragma unroll
       for (int d = 0; d < DEPTH; ++d) step(ring[d], LD);
@@ -686,10 +688,7 @@ __global__ __launch_bounds__(64 * NW * SG) void q2_0_pairs_kernel(const uint16_t
   };
   if (rem >= (uint32_t)DEPTH) {
     const uint32_t e = rem - DEPTH;  // < DEPTH
-    if (e == 0u)
-      drain(std::integral_constant<int, 0>{});
-    else
-      drain(std::integral_constant<int, 1>{});
+    drain_case<0, DEPTH>(e, drain);
   } else {  // fewer units than the ring (the prologue requested a few past the end)
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d)
@@ -828,28 +827,38 @@ hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32
     // the staging barrier: N = K = 5120 M = 2: 4.86 -> 4.71 us, N = 5120
     // K = 17408 M = 1: 9.92 -> 9.33).
     //
-    // The scale by its own load for one row under 16 MB, else from the code
-    // window of the column's first lane (the same bits; measured on MI355X,
-    // interleaved A/B: N = K = 5120, M = 1 4.47 against 4.49 us with the
-    // permute, N = 256 K = 1024 2.33 against 2.36; with the permute N = 5120
-    // K = 17408 M = 1 9.32 -> 8.92 us, N = K = 5120 M = 2 4.70 -> 4.62, M = 8
-    // 6.71 -> 6.61).
+    // One row: the scale from the code window of the column's first lane, no
+    // request past a wave's last unit, and a ring as deep as the pairs a wave
+    // owns per tile when that is three (K = 4352 .. 6144), else two with the
+    // second requested after the staging barrier (the third, on large
+    // matrices); the same bits every way.  Measured on MI355X (interleaved
+    // A/B, graph-replayed, against the earlier two-deep ring with a separate
+    // scale load and requests past the end): N = K = 5120 4.48 -> 4.32 us
+    // (two-deep drained 4.38, with the second late 4.35), N = K = 4096
+    // 4.02 -> 3.58, N = K = 2048 2.69 -> 2.54, N = 256 K = 1024 2.31 -> 2.26,
+    // N = 8192 K = 8192 7.23 -> 6.92, N = 17408 K = 5120 8.43 -> 8.16.
     if constexpr (MMAX == 1) {
-      if (!big) {
-        if (per_thread <= 2) return launch_persistent<q2_0_pairs_kernel<1, NW, 2, 2, false, 1, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
-        if (per_thread <= 3) return launch_persistent<q2_0_pairs_kernel<1, NW, 2, 3, false, 1, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
-        if (per_thread <= 4) return launch_persistent<q2_0_pairs_kernel<1, NW, 2, 4, false, 1, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
-        if (per_thread <= 5) return launch_persistent<q2_0_pairs_kernel<1, NW, 2, 5, false, 1, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
-        return launch_persistent<q2_0_pairs_kernel<1, NW, 2, 10, false, 1, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
-      }
+      const uint32_t pairs_per_wave = ((K >> 8) + NW - 1u) / NW;
+#define WQD_M1(D, L)                                                                                                      \
+  do {                                                                                                                    \
+    if (per_thread <= 2) return launch_persistent<q2_0_pairs_kernel<1, NW, D, 2, false, 1, L, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M); \
+    if (per_thread <= 3) return launch_persistent<q2_0_pairs_kernel<1, NW, D, 3, false, 1, L, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M); \
+    if (per_thread <= 4) return launch_persistent<q2_0_pairs_kernel<1, NW, D, 4, false, 1, L, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M); \
+    if (per_thread <= 5) return launch_persistent<q2_0_pairs_kernel<1, NW, D, 5, false, 1, L, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M); \
+    return launch_persistent<q2_0_pairs_kernel<1, NW, D, 10, false, 1, L, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M); \
+  } while (0)
+      if (pairs_per_wave == 3u && !big) WQD_M1(3, 0);
+      if (pairs_per_wave == 3u) WQD_M1(3, 1);
+      WQD_M1(2, 1);
+#undef WQD_M1
     }
     if (!wfirst) {
       {
-        if (per_thread <= 2) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 2, false>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
-        if (per_thread <= 3) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 3, false>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
-        if (per_thread <= 4) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 4, false>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
-        if (per_thread <= 5) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 5, false>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
-        return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 10, false>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
+        if (per_thread <= 2) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 2, false, 1, 0, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
+        if (per_thread <= 3) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 3, false, 1, 0, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
+        if (per_thread <= 4) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 4, false, 1, 0, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
+        if (per_thread <= 5) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 5, false, 1, 0, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
+        return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 10, false, 1, 0, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
       }
     }
     if (per_thread <= 2) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, kDepth, 2, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
