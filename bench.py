@@ -350,7 +350,7 @@ def cpu_threads() -> int:
 
 
 # The headline's kernel and the committed rocprofv3 summary that covers it.
-HEADLINE_KERNEL = {"name": "q2_0_pairs_kernel<1, 8, 3, 2, false, 1, 0, true>", "source": "q2_0_mfma.hip",
+HEADLINE_KERNEL = {"name": "q2_0_pairs_kernel<1, 8, 3, 2, 1, 0>", "source": "q2_0_mfma.hip",
                    "profile": "q2_0_gemv_kernel_m1_5120x5120"}
 
 

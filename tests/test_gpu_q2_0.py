@@ -167,13 +167,15 @@ def test_large_k_batched_rows(oracle_mod, N, K, M):
 @pytest.mark.parametrize("N,K,M", [(5120, 5120, 3), (17408, 5120, 3), (17408, 5120, 4), (5120, 17408, 2),
                                    (5120, 17408, 3), (5120, 17408, 4), (4100, 5120, 3), (2052, 17408, 2)])
 def test_two_to_four_rows_every_staging_tier(oracle_mod, N, K, M):
-    """Two to four rows run at two workgroups per compute unit, activations
-    requested first below 16 MB of weights and weights first above, with 2, 3,
-    4, 5 or 10 staging chunks per thread (M = 3 at K = 5120 takes 4, M = 4 at
-    K = 5120 takes 5, M = 2..4 at K = 17408 take 10 over one or two rounds);
-    ragged N (4100 and 2052 end in a partial tile).  Every row bit-identical
-    to its own M=1 launch, a canary row past M untouched, a column sample
-    within tolerance of the oracle."""
+    """Two to four rows run at two workgroups per compute unit with a two-deep
+    ring below 16 MB of weights, and at one with a three-deep ring whose third
+    request follows the staging barrier above (and at K = 17408, N = 2052,
+    where two copies of the activations do not fit in LDS), with 2, 3, 4, 5 or
+    10 staging chunks per thread (M = 3 at K = 5120 takes 4, M = 4 at K = 5120
+    takes 5, M = 2..4 at K = 17408 take 10 over one or two rounds); ragged N
+    (4100 and 2052 end in a partial tile).  Every row bit-identical to its own
+    M=1 launch, a canary row past M untouched, a column sample within
+    tolerance of the oracle."""
     A, codes, d, packed = _case(41, N, K, M, salt=N * 7 + K + M)
     Bd = dev_u8(packed)
     got = q2_0_gpu(A, Bd, N, K, extra_rows=1)

@@ -422,7 +422,7 @@ __device__ __forceinline__ void drain_case(uint32_t e, F &&f) {
   }
 }
 
-template <int MMAX, int NW, int DEPTH, int UA, bool WFIRST, int SG = 1, int LATE = 0, bool DRN = false>
+template <int MMAX, int NW, int DEPTH, int UA, int SG = 1, int LATE = 0>
 __global__ __launch_bounds__(64 * NW * SG) void q2_0_pairs_kernel(const uint16_t *__restrict__ A,
                                                                   const uint8_t *__restrict__ B,
                                                                   uint16_t *__restrict__ C, uint32_t N, uint32_t K,
@@ -465,11 +465,11 @@ __global__ __launch_bounds__(64 * NW * SG) void q2_0_pairs_kernel(const uint16_t
       adst[u] = in ? a_off + 16u * (cc + m) : (uint32_t)L::kPart;
     }
   };
-  // Activations first (WFIRST false): their first round is requested before
-  // any other set-up (about 100 mostly scalar instructions per wave, which the
-  // waves of a CU issue one at a time on its scalar unit); measured on MI355X
-  // at N = K = 5120, M = 1: 4.87 -> 4.48 us per call.
-  if constexpr (!WFIRST) a_load(0u);
+  // The activations' first round is requested before any other set-up (about
+  // 100 mostly scalar instructions per wave, which the waves of a CU issue one
+  // at a time on its scalar unit); measured on MI355X at N = K = 5120, M = 1:
+  // 4.87 -> 4.48 us per call.
+  a_load(0u);
 
   const uint32_t rb = nb * kBlockBytes;
   const uint32_t ntiles = N >= (uint32_t)kRows ? (N + kRows - 1u) / kRows : 1u;
@@ -491,7 +491,6 @@ __global__ __launch_bounds__(64 * NW * SG) void q2_0_pairs_kernel(const uint16_t
       *reinterpret_cast<u32x4_t *>(lds + L::kZero + 16u * tid) = z;
     }
   };
-  if constexpr (WFIRST) zero_rows();
   const __amdgpu_buffer_rsrc_t wrsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(B), (short)0, (int)(N * rb), 0x00020000);
   const uint32_t row_off = min(rw, N - 1u) * rb;  // rows past N (N < 8) re-read row N - 1
@@ -543,18 +542,10 @@ __global__ __launch_bounds__(64 * NW * SG) void q2_0_pairs_kernel(const uint16_t
 #pragma unroll
       for (int u = 0; u < UA; ++u) *reinterpret_cast<u32x4_t *>(lds + adst[u]) = permute_acts(av[u]);
     };
-    // WFIRST: the first pairs' weights are requested before the activations
-    // (faster for 5..8 rows, and for batched rows of large matrices);
-    // otherwise after them (the launcher's choice for one row and for 2..4
-    // rows of a small matrix, where the activation copy is on
-    // the critical path)
+    // the first DEPTH - LATE pairs' weights, behind the activations' first round
 #pragma unroll
     for (int d = 0; d < DEPTH - LATE; ++d) ring[d] = issue_next();
-    if constexpr (WFIRST) {
-      a_load(0u);
-    } else {
-      zero_rows();
-    }
+    zero_rows();
     a_store();
     for (uint32_t base = UA * (64u * NW * SG); base < total; base += UA * (64u * NW * SG)) {
       a_load(base);
@@ -648,27 +639,15 @@ __global__ __launch_bounds__(64 * NW * SG) void q2_0_pairs_kernel(const uint16_t
     }
   };
 
-  // DRN: only units the wave computes are requested.  The loop runs while
-  // all of its requests are, and the DEPTH..2 DEPTH - 1 units left after it
-  // run as straight-line code with exactly the requests still needed (a
-  // request past the wave's last unit occupies the compute unit's address
-  // path; one behind a branch makes the compiler wait for every load in
-  // flight where the branch rejoins).  Without DRN the ring requests units
-  // past the end (re-reading the wave's first pair), which measured better
-  // for the three-deep weights-first ring of five to eight rows (M = 8: 6.59
-  // against 6.77 us drained).
+  // Only units the wave computes are requested.  The loop runs while all of
+  // its requests are, and the DEPTH .. 2 DEPTH - 1 units left after it run as
+  // straight-line code with exactly the requests still needed (a request past
+  // the wave's last unit occupies the compute unit's address path; one behind
+  // a branch makes the compiler wait for every load in flight where the
+  // branch rejoins).  Measured on MI355X against a ring that requests units
+  // past the end: N = K = 5120 M = 2 4.63 -> 4.52 us, M = 4 5.00 -> 4.87.
   const std::true_type LD;
   const std::false_type NOLD;
-  if constexpr (!DRN) {
-    while (cc.q + DEPTH <= nq) {
-#pragma unroll
-      for (int d = 0; d < DEPTH; ++d) step(ring[d], LD);
-    }
-#pragma unroll
-    for (int d = 0; d < DEPTH; ++d)
-      if (cc.q < nq) step(ring[d], LD);
-    return;
-  }
   while (cc.q + 2u * DEPTH <= nq) {
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) step(ring[d], LD);
@@ -777,18 +756,36 @@ hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32
   const auto *b = static_cast<const uint8_t *>(B);
   auto *c = static_cast<uint16_t *>(C);
   constexpr int NW = 8;
-  // Measured on MI355X (graph-replayed, cold weights, N = K = 5120 unless
-  // stated): two block pairs in flight per wave with the activations
-  // requested first, three for batched rows that request the weights first
-  // (N = 17408, M = 8: 13.8 -> 12.5 us; at M = 1 three cost 5.28 -> 5.54);
-  // and up to two workgroups per compute unit where the LDS allows it (M = 1:
-  // 5.28 -> 4.88 us, N = 5120 K = 17408: 12.1 -> 10.6; M = 5: 6.58 -> 5.91,
-  // M = 7: 6.70 -> 6.16, with the activations requested first), except for
-  // five to eight rows of a matrix of 16 MB or more (one, in two subgroups).
-  constexpr int kDepth = 3;  // weights first
   const bool bounded = (uint64_t)N * (K >> 7) * kBlockBytes < (1ull << 32);  // buffer-load range
   const bool big = (uint64_t)N * (K >> 7) * kBlockBytes >= (16ull << 20);
+  // Up to two workgroups per compute unit where the LDS allows it (measured
+  // on MI355X, graph-replayed, cold weights: M = 1 5.28 -> 4.88 us at
+  // N = K = 5120, N = 5120 K = 17408 12.1 -> 10.6; M = 5 6.58 -> 5.91, M = 7
+  // 6.70 -> 6.16), except for five to eight rows of a matrix of 16 MB or more.
   const int kMaxPerCu = (MMAX <= 4 || !big) ? 2 : 1;
+  // Ring schedules (the same bits whatever the schedule): every launch
+  // requests its activations first and drains its ring without requests past
+  // a wave's last unit.  A wave keeps DEPTH block pairs in flight, LATE of the
+  // first DEPTH requested only after the staging barrier (so that they do not
+  // queue ahead of the activation copy).
+  //   * One row: three pairs when a wave owns three per tile (K = 4352 ..
+  //     6144; the third late on large matrices), else two with the second
+  //     late.  Measured against two with a separate scale load and requests
+  //     past the end: N = K = 5120 4.48 -> 4.32 us (two-deep drained 4.38,
+  //     with the second late 4.35), N = K = 4096 4.02 -> 3.58, N = K = 2048
+  //     2.69 -> 2.54, N = 256 K = 1024 2.31 -> 2.26, N = K = 8192 7.23 ->
+  //     6.92, N = 17408 K = 5120 8.43 -> 8.16.
+  //   * Batched rows with two workgroups per compute unit: two pairs.
+  //   * Batched rows with one workgroup per compute unit (matrices of 16 MB or
+  //     more, or five to eight rows whose activations leave LDS for one):
+  //     three pairs, the third late.  Measured against three with the
+  //     weights requested before the activations and requests past the end:
+  //     N = K = 5120 M = 8 6.60 -> 6.46 us, N = K = 8192 M = 2 8.25 -> 7.61,
+  //     M = 4 9.80 -> 8.87, N = 17408 K = 5120 M = 2 9.40 -> 8.57, M = 3 9.84 ->
+  //     9.08, M = 4 10.47 -> 9.59, N = 5120 K = 17408 M = 2 10.77 -> 10.11,
+  //     M = 4 12.94 -> 12.53; two subgroups (below) N = 17408 K = 5120 M = 5
+  //     11.67 -> 10.97, M = 8 11.30 -> 10.61.
+  //
   // Five to eight rows of a matrix of 16 MB or more: two subgroups of 8 waves
   // per workgroup over one copy of the activations (measured on MI355X,
   // N = 17408, K = 5120: M = 8 12.45 -> 11.46 us, M = 5 12.54 -> 11.70; at
@@ -800,72 +797,38 @@ hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32
     if (big && lds2 <= kLdsMax && bounded) {
       const uint32_t pt = (M * (K >> 3) + 1023u) / 1024u;
       const uint32_t half = (ntiles + 1u) / 2u;
-      if (pt <= 2) return launch_persistent<q2_0_pairs_kernel<8, NW, kDepth, 2, true, 2>>(1024, lds2, 1, half, stream, a, b, c, N, K, M);
-      if (pt <= 3) return launch_persistent<q2_0_pairs_kernel<8, NW, kDepth, 3, true, 2>>(1024, lds2, 1, half, stream, a, b, c, N, K, M);
-      if (pt <= 5) return launch_persistent<q2_0_pairs_kernel<8, NW, kDepth, 5, true, 2>>(1024, lds2, 1, half, stream, a, b, c, N, K, M);
-      return launch_persistent<q2_0_pairs_kernel<8, NW, kDepth, 10, true, 2>>(1024, lds2, 1, half, stream, a, b, c, N, K, M);
+      if (pt <= 2) return launch_persistent<q2_0_pairs_kernel<8, NW, 3, 2, 2, 1>>(1024, lds2, 1, half, stream, a, b, c, N, K, M);
+      if (pt <= 3) return launch_persistent<q2_0_pairs_kernel<8, NW, 3, 3, 2, 1>>(1024, lds2, 1, half, stream, a, b, c, N, K, M);
+      if (pt <= 5) return launch_persistent<q2_0_pairs_kernel<8, NW, 3, 5, 2, 1>>(1024, lds2, 1, half, stream, a, b, c, N, K, M);
+      return launch_persistent<q2_0_pairs_kernel<8, NW, 3, 10, 2, 1>>(1024, lds2, 1, half, stream, a, b, c, N, K, M);
     }
   }
   const size_t lds = pair_lds_bytes<MMAX>(M, K);
   if (lds <= kLdsMax && bounded) {  // activations fit in LDS: the pairs kernel
-    // activation chunks per thread for one staging round covering all of A
-    const uint32_t per_thread = (M * (K >> 3) + 64 * NW - 1) / (64 * NW);
-    // Activations first (their first round requested before any other
-    // set-up), or the first pairs' weights first.  Measured on MI355X
-    // (interleaved A/B, graph-replayed): activations first for one row at any
-    // size (N = 17408, K = 5120: 8.94 -> 8.48 us; N = 5120, K = 17408:
-    // 10.41 -> 9.95), for 2..4 rows of a matrix under 16 MB (N = K = 5120,
-    // M = 2: 5.53 -> 4.86 us, M = 4: 6.68 -> 6.30) and for 5..7 rows there
-    // when two workgroups share a compute unit; weights first for a lone
-    // workgroup per compute unit (N = K = 5120, M = 8: 6.62 against 6.70 us)
-    // and for batched rows of larger matrices (N = 17408, M = 8: 12.5 against
-    // 13.7 us).
-    const bool two_per_cu = kMaxPerCu >= 2 && 2u * lds <= kLdsMax;
-    const bool wfirst = M > 1 && (big || (M > 4 && !two_per_cu));
     // Staging chunks per thread: the smallest of 2, 3, 4, 5 and 10 that
     // covers A in one round (idle chunk slots cost loads and registers before
     // the staging barrier: N = K = 5120 M = 2: 4.86 -> 4.71 us, N = 5120
     // K = 17408 M = 1: 9.92 -> 9.33).
-    //
-    // One row: the scale from the code window of the column's first lane, no
-    // request past a wave's last unit, and a ring as deep as the pairs a wave
-    // owns per tile when that is three (K = 4352 .. 6144), else two with the
-    // second requested after the staging barrier (the third, on large
-    // matrices); the same bits every way.  Measured on MI355X (interleaved
-    // A/B, graph-replayed, against the earlier two-deep ring with a separate
-    // scale load and requests past the end): N = K = 5120 4.48 -> 4.32 us
-    // (two-deep drained 4.38, with the second late 4.35), N = K = 4096
-    // 4.02 -> 3.58, N = K = 2048 2.69 -> 2.54, N = 256 K = 1024 2.31 -> 2.26,
-    // N = 8192 K = 8192 7.23 -> 6.92, N = 17408 K = 5120 8.43 -> 8.16.
+    const uint32_t per_thread = (M * (K >> 3) + 64 * NW - 1) / (64 * NW);
+#define WQD_PAIRS(D, L)                                                                                                   \
+  do {                                                                                                                    \
+    if (per_thread <= 2) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, D, 2, 1, L>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M); \
+    if (per_thread <= 3) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, D, 3, 1, L>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M); \
+    if (per_thread <= 4) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, D, 4, 1, L>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M); \
+    if (per_thread <= 5) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, D, 5, 1, L>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M); \
+    return launch_persistent<q2_0_pairs_kernel<MMAX, NW, D, 10, 1, L>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M); \
+  } while (0)
     if constexpr (MMAX == 1) {
       const uint32_t pairs_per_wave = ((K >> 8) + NW - 1u) / NW;
-#define WQD_M1(D, L)                                                                                                      \
-  do {                                                                                                                    \
-    if (per_thread <= 2) return launch_persistent<q2_0_pairs_kernel<1, NW, D, 2, false, 1, L, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M); \
-    if (per_thread <= 3) return launch_persistent<q2_0_pairs_kernel<1, NW, D, 3, false, 1, L, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M); \
-    if (per_thread <= 4) return launch_persistent<q2_0_pairs_kernel<1, NW, D, 4, false, 1, L, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M); \
-    if (per_thread <= 5) return launch_persistent<q2_0_pairs_kernel<1, NW, D, 5, false, 1, L, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M); \
-    return launch_persistent<q2_0_pairs_kernel<1, NW, D, 10, false, 1, L, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M); \
-  } while (0)
-      if (pairs_per_wave == 3u && !big) WQD_M1(3, 0);
-      if (pairs_per_wave == 3u) WQD_M1(3, 1);
-      WQD_M1(2, 1);
-#undef WQD_M1
+      if (pairs_per_wave == 3u && !big) WQD_PAIRS(3, 0);
+      if (pairs_per_wave == 3u) WQD_PAIRS(3, 1);
+      WQD_PAIRS(2, 1);
+    } else {
+      const bool two_per_cu = kMaxPerCu >= 2 && 2u * lds <= kLdsMax;
+      if (two_per_cu && !big) WQD_PAIRS(2, 0);
+      WQD_PAIRS(3, 1);
     }
-    if (!wfirst) {
-      {
-        if (per_thread <= 2) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 2, false, 1, 0, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
-        if (per_thread <= 3) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 3, false, 1, 0, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
-        if (per_thread <= 4) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 4, false, 1, 0, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
-        if (per_thread <= 5) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 5, false, 1, 0, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
-        return launch_persistent<q2_0_pairs_kernel<MMAX, NW, 2, 10, false, 1, 0, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
-      }
-    }
-    if (per_thread <= 2) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, kDepth, 2, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
-    if (per_thread <= 3) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, kDepth, 3, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
-    if (per_thread <= 4) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, kDepth, 4, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
-    if (per_thread <= 5) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, kDepth, 5, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
-    return launch_persistent<q2_0_pairs_kernel<MMAX, NW, kDepth, 10, true>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M);
+#undef WQD_PAIRS
   }
   // else per phase (same bits)
   return launch_phase<MMAX>(a, b, c, N, K, M, stream);
