@@ -21,11 +21,11 @@
 //     leaves room for all 8 activation rows of a batched launch.
 //   * A workgroup of 8 waves walks its tiles (blockIdx.x, + gridDim.x, ...).
 //     Wave w owns block pairs w, w+8, w+16, ... of every tile and works on
-//     its own: for each pair it fetches the 8 rows' 68 bytes (5 aligned
-//     16-byte chunks per row, one load per lane), keeps DEPTH pairs in flight
-//     in registers, and passes them through its own LDS buffers to the lanes
-//     that need them.  No barrier separates a wave's loads from its compute;
-//     the 8 waves meet once per tile, to add their partial sums.
+//     its own: for each pair every lane loads the 12-byte window of the 8
+//     rows' 68 bytes that holds its own 8 code bytes (one buffer load per
+//     lane, straight into the registers the decode reads), and the wave keeps
+//     DEPTH pairs in flight.  No barrier separates a wave's loads from its
+//     compute; the 8 waves meet once per tile, to add their partial sums.
 //   * Activations: all M rows of A are copied into LDS once per workgroup.
 //     Each group of four consecutive activations is stored in the order
 //     (a0, a2, a1, a3), the order the decode below produces codes in.  Rows
@@ -74,7 +74,6 @@ constexpr int kSlots8 = 8;  // accumulation slots of a tile's block pairs
 constexpr int kPhaseBlocks = 16;                          // blocks per phase (8 waves x 2)
 constexpr int kPhaseRowBytes = kPhaseBlocks * kBlockBytes;  // 544 bytes of one weight row per phase
 constexpr int kWPitch = kPhaseRowBytes + 16;              // LDS row pitch (bank spread)
-constexpr int kWBytes = kRows * kWPitch;                  // weight part of a buffer
 constexpr int kAPhaseBytes = kPhaseBlocks * 256;          // 4096 bytes of one activation row per phase
 constexpr int kAPitch = kAPhaseBytes + 16;                // LDS pitch of a per-phase activation row
 constexpr uint32_t kLdsMax = 160u * 1024u;                // LDS per compute unit on gfx950
@@ -498,8 +497,11 @@ __global__ __launch_bounds__(64 * NW * SG) void q2_0_pairs_kernel(const uint16_t
   // Unit q of this wave is pair wave + NW*u of tile j (q = j * upw + u).
   // Two wave-uniform cursors walk the units in order, one for the loads
   // (DEPTH units ahead) and one for the compute, so the per-unit bookkeeping
-  // is a few scalar adds.  Past the end the load cursor re-reads the wave's
-  // first pair (clamped into the row), which is never used.
+  // is a few scalar adds.  Past the end the load cursor keeps walking with its
+  // tile rows clamped to the last tile, so the load address never waits for
+  // the tile count (a division); such loads are never used.  Measured on
+  // MI355X against re-reading the wave's first pair past the end: N = 17408
+  // K = 5120 M = 1 8.19 -> 8.09 us, N = K = 5120 M = 8 6.44 -> 6.39.
   struct Cursor {
     uint32_t q, u, j, row;  // unit, pair index within the tile, tile index, tile's first row
   };
@@ -514,11 +516,10 @@ __global__ __launch_bounds__(64 * NW * SG) void q2_0_pairs_kernel(const uint16_t
       c.row = N >= (uint32_t)kRows ? min(c.row + row_step, row_last) : 0u;
     }
   };
-  const uint32_t soff_first = first_row() * rb + 68u * min(wave, npairs - 1u);
   Cursor ld = {0u, 0u, 0u, first_row()};
   auto issue_next = [&]() {
     const uint32_t p = min(wave + NW * ld.u, npairs - 1u);
-    const uint32_t soff = ld.q < nq ? ld.row * rb + 68u * p : soff_first;
+    const uint32_t soff = ld.row * rb + 68u * p;
     PairRegs r;
     r.w = __builtin_amdgcn_raw_buffer_load_b96(wrsrc, w_voff, soff, 0);
     advance(ld);
