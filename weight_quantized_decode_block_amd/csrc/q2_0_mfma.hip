@@ -710,6 +710,26 @@ hipError_t launch_persistent(int threads, size_t lds, int max_per_cu, uint32_t n
   return hipGetLastError();
 }
 
+// The pairs kernel with UA = the activation chunks per thread that cover A in
+// one staging round exactly (1 .. 10; larger A is staged in rounds of 10).
+// Idle chunk slots (which re-read chunk 0 and are stored nowhere useful) cost
+// time: measured on MI355X against the coarser choice of 2, 3, 4, 5 or 10,
+// N = K = 5120 M = 5 5.88 -> 5.42 us, M = 6 5.92 -> 5.70, N = K = 4096 M = 1
+// 3.55 -> 3.49 (and against 10 everywhere, N = K = 5120 M = 2 4.86 -> 4.71,
+// N = 5120 K = 17408 M = 1 9.92 -> 9.33).
+template <int MMAX, int NW, int D, int SG, int LATE, int UA = 1>
+hipError_t launch_pairs(uint32_t per_thread, int threads, size_t lds, int max_per_cu, uint32_t ntiles,
+                        hipStream_t stream, const uint16_t *a, const uint8_t *b, uint16_t *c, uint32_t N, uint32_t K,
+                        uint32_t M) {
+  if constexpr (UA < 10) {
+    if (per_thread > (uint32_t)UA)
+      return launch_pairs<MMAX, NW, D, SG, LATE, UA + 1>(per_thread, threads, lds, max_per_cu, ntiles, stream, a, b, c,
+                                                          N, K, M);
+  }
+  return launch_persistent<q2_0_pairs_kernel<MMAX, NW, D, UA, SG, LATE>>(threads, lds, max_per_cu, ntiles, stream, a, b,
+                                                                         c, N, K, M);
+}
+
 template <int MMAX, int TPP>
 hipError_t launch_phase_tpp(uint32_t grid, hipStream_t stream, const uint16_t *a, const uint8_t *b, uint16_t *c,
                             uint32_t N, uint32_t K, uint32_t M) {
@@ -798,27 +818,14 @@ hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32
     if (big && lds2 <= kLdsMax && bounded) {
       const uint32_t pt = (M * (K >> 3) + 1023u) / 1024u;
       const uint32_t half = (ntiles + 1u) / 2u;
-      if (pt <= 2) return launch_persistent<q2_0_pairs_kernel<8, NW, 3, 2, 2, 1>>(1024, lds2, 1, half, stream, a, b, c, N, K, M);
-      if (pt <= 3) return launch_persistent<q2_0_pairs_kernel<8, NW, 3, 3, 2, 1>>(1024, lds2, 1, half, stream, a, b, c, N, K, M);
-      if (pt <= 5) return launch_persistent<q2_0_pairs_kernel<8, NW, 3, 5, 2, 1>>(1024, lds2, 1, half, stream, a, b, c, N, K, M);
-      return launch_persistent<q2_0_pairs_kernel<8, NW, 3, 10, 2, 1>>(1024, lds2, 1, half, stream, a, b, c, N, K, M);
+      return launch_pairs<8, NW, 3, 2, 1>(pt, 1024, lds2, 1, half, stream, a, b, c, N, K, M);
     }
   }
   const size_t lds = pair_lds_bytes<MMAX>(M, K);
   if (lds <= kLdsMax && bounded) {  // activations fit in LDS: the pairs kernel
-    // Staging chunks per thread: the smallest of 2, 3, 4, 5 and 10 that
-    // covers A in one round (idle chunk slots cost loads and registers before
-    // the staging barrier: N = K = 5120 M = 2: 4.86 -> 4.71 us, N = 5120
-    // K = 17408 M = 1: 9.92 -> 9.33).
-    const uint32_t per_thread = (M * (K >> 3) + 64 * NW - 1) / (64 * NW);
-#define WQD_PAIRS(D, L)                                                                                                   \
-  do {                                                                                                                    \
-    if (per_thread <= 2) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, D, 2, 1, L>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M); \
-    if (per_thread <= 3) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, D, 3, 1, L>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M); \
-    if (per_thread <= 4) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, D, 4, 1, L>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M); \
-    if (per_thread <= 5) return launch_persistent<q2_0_pairs_kernel<MMAX, NW, D, 5, 1, L>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M); \
-    return launch_persistent<q2_0_pairs_kernel<MMAX, NW, D, 10, 1, L>>(64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M); \
-  } while (0)
+    const uint32_t per_thread = (M * (K >> 3) + 64 * NW - 1) / (64 * NW);  // staging chunks per thread
+#define WQD_PAIRS(D, L) \
+  return launch_pairs<MMAX, NW, D, 1, L>(per_thread, 64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M)
     if constexpr (MMAX == 1) {
       const uint32_t pairs_per_wave = ((K >> 8) + NW - 1u) / NW;
       if (pairs_per_wave == 3u && !big) WQD_PAIRS(3, 0);
