@@ -272,3 +272,25 @@ def test_two_deep_ring_drain_unit_counts(oracle_mod, N, K, M):
         assert np.array_equal(got[m:m + 1], q2_0_gpu(A[m:m + 1], Bd, N, K, single=True)), m
     cols = np.arange(N) if N <= 400 else np.union1d(gen.rng(959, N, K).choice(N, 256, replace=False), [N - 1])
     check_parity(got[:, cols], oracle_mod.q2_0_gemv(A, codes[cols], d[cols]), f"q2_0 {N}x{K} M={M}")
+
+
+@pytest.mark.parametrize("N,K,M", [(520, 4096, 1), (520, 4096, 2), (264, 4096, 3), (264, 4096, 4), (136, 4096, 5),
+                                   (136, 4096, 6), (72, 4096, 7), (72, 4096, 8), (1040, 12288, 3), (200, 8192, 5),
+                                   (264, 6144, 8), (130, 2048, 1)])
+def test_every_staging_width(oracle_mod, N, K, M):
+    """The activation copy gives each thread exactly the 16-byte chunks that
+    cover A in one round: M * K / 4096 of them here, every width from 1 to 10
+    (K = 4096 at M = 1..8, K = 12288 at M = 3, K = 8192 at M = 5), more than
+    one round (K = 6144 at M = 8: 12 chunks, two rounds of 10) and a round
+    with idle slots (K = 2048 at M = 1).  Every row equals its own M=1 launch,
+    a canary row past M stays untouched and the outputs are within tolerance
+    of the oracle."""
+    print(f"staging N={N} K={K} M={M}", flush=True)
+    A, codes, d, packed = _case(61, N, K, M, salt=N * 7 + K + M)
+    Bd = dev_u8(packed)
+    got = q2_0_gpu(A, Bd, N, K, extra_rows=1)
+    assert np.all(got[M] == CANARY)
+    got = got[:M]
+    for m in range(M):
+        assert np.array_equal(got[m:m + 1], q2_0_gpu(A[m:m + 1], Bd, N, K, single=True)), m
+    check_parity(got, oracle_mod.q2_0_gemv(A, codes, d), f"q2_0 {N}x{K} M={M}")
