@@ -352,7 +352,7 @@ __global__ __launch_bounds__(kThreads) void q2_0_phase_kernel(const uint16_t *__
           const float *pp = part + ((par * TPP + t) * kWaves * 2u * MMAX + m) * kRows + r;
           float v = pp[0];
           for (uint32_t k = 1; k < 2u * kWaves; ++k) v = v + pp[k * MMAX * kRows];
-          C[(size_t)m * N + n] = f32_to_bf16_rne(v);
+          store_out(C + (size_t)m * N + n, f32_to_bf16_rne(v));
         }
       }
       // the next write of this parity's partials comes after another super-tile's barriers
@@ -633,7 +633,7 @@ __global__ __launch_bounds__(64 * NW * SG) void q2_0_pairs_kernel(const uint16_t
           const float *pp = part + (par * kSlots8 * 2u * MMAX + m) * kRows + col;
           float v = pp[0];
           for (uint32_t k = 1; k < 2u * kSlots8; ++k) v = v + pp[k * MMAX * kRows];
-          C[(size_t)m * N + n] = f32_to_bf16_rne(v);
+          store_out(C + (size_t)m * N + n, f32_to_bf16_rne(v));
         }
       }
       // this parity's partials are next written after the following tile's barrier
