@@ -554,18 +554,22 @@ inline hipError_t unit_scales_fit(uint32_t N, uint32_t K, uint32_t band, bool &f
   return hipSuccess;
 }
 
-template <int MMAX, bool SL>
+// Staging chunks per thread: exactly the number that covers A in one round
+// (1 .. 10; larger A is staged in rounds of 10).  Idle chunk slots re-read
+// chunk 0 before the staging barrier; measured on MI355X against the coarser
+// choice of 2, 3, 4, 5 or 10: N = K = 5120 M = 5 8.77 -> 8.46 us, M = 6
+// 8.81 -> 8.57, M = 7 8.87 -> 8.78, N = 17408 K = 5120 M = 5 19.45 -> 19.14
+// (and that choice against 10 everywhere: N = K = 5120 M = 4 8.71 -> 8.42,
+// N = 5120 K = 17408 M = 1 20.5 -> 20.1).
+template <int MMAX, bool SL, int UA = 1>
 hipError_t launch_units_sl(uint32_t per_thread, size_t lds, uint32_t ntiles, uint32_t band, hipStream_t stream,
                            const uint16_t *a, const uint8_t *w, const float *S, uint16_t *c, uint32_t M, uint32_t N,
                            uint32_t K, uint32_t lda, uint32_t ldc) {
-  // staging chunks per thread: the smallest of 2, 3, 4, 5 and 10 covering A in
-  // one round (measured on MI355X: N = K = 5120 M = 4: 8.71 -> 8.42 us;
-  // N = 5120 K = 17408 M = 1: 20.5 -> 20.1)
-  if (per_thread <= 2) return launch_units<w8a16_units_kernel<MMAX, 4, 2, SL>>(lds, ntiles, band, stream, a, w, S, c, M, N, K, lda, ldc);
-  if (per_thread <= 3) return launch_units<w8a16_units_kernel<MMAX, 4, 3, SL>>(lds, ntiles, band, stream, a, w, S, c, M, N, K, lda, ldc);
-  if (per_thread <= 4) return launch_units<w8a16_units_kernel<MMAX, 4, 4, SL>>(lds, ntiles, band, stream, a, w, S, c, M, N, K, lda, ldc);
-  if (per_thread <= 5) return launch_units<w8a16_units_kernel<MMAX, 4, 5, SL>>(lds, ntiles, band, stream, a, w, S, c, M, N, K, lda, ldc);
-  return launch_units<w8a16_units_kernel<MMAX, 4, 10, SL>>(lds, ntiles, band, stream, a, w, S, c, M, N, K, lda, ldc);
+  if constexpr (UA < 10) {
+    if (per_thread > (uint32_t)UA)
+      return launch_units_sl<MMAX, SL, UA + 1>(per_thread, lds, ntiles, band, stream, a, w, S, c, M, N, K, lda, ldc);
+  }
+  return launch_units<w8a16_units_kernel<MMAX, 4, UA, SL>>(lds, ntiles, band, stream, a, w, S, c, M, N, K, lda, ldc);
 }
 
 template <int MMAX>
