@@ -170,9 +170,9 @@ def test_two_to_four_rows_every_staging_tier(oracle_mod, N, K, M):
     """Two to four rows run at two workgroups per compute unit with a two-deep
     ring below 16 MB of weights, and at one with a three-deep ring whose third
     request follows the staging barrier above (and at K = 17408, N = 2052,
-    where two copies of the activations do not fit in LDS), with 2, 3, 4, 5 or
-    10 staging chunks per thread (M = 3 at K = 5120 takes 4, M = 4 at K = 5120
-    takes 5, M = 2..4 at K = 17408 take 10 over one or two rounds); ragged N
+    where two copies of the activations do not fit in LDS), with the staging
+    chunks per thread that cover A (M = 3 at K = 5120 takes 4, M = 4 takes 5,
+    M = 2 at K = 17408 takes 9, M = 3 and 4 there two rounds of 10); ragged N
     (4100 and 2052 end in a partial tile).  Every row bit-identical to its own
     M=1 launch, a canary row past M untouched, a column sample within
     tolerance of the oracle."""
