@@ -387,6 +387,17 @@ constexpr size_t pair_lds_bytes(uint32_t M, uint32_t K) {
   return (size_t)PairLayout<MMAX, SG>::kFixed + (size_t)SG * (K >> 7) * 32u + (size_t)M * (2u * K + 16u);
 }
 
+// f(integral_constant<e>) for the runtime value e in [E, D)
+template <int E, int D, typename F>
+__device__ __forceinline__ void drain_case(uint32_t e, F &&f) {
+  if constexpr (E < D) {
+    if (e == (uint32_t)E)
+      f(std::integral_constant<int, E>{});
+    else
+      drain_case<E + 1, D>(e, f);
+  }
+}
+
 // One block pair's bytes for this lane: the aligned 3-dword window holding
 // its 8 code bytes.  The fp16 scale comes from the window of lane g = 0 of
 // the same column, which starts at the half's scale (first block) or two
@@ -410,17 +421,6 @@ struct PairRegs {
 // barrier is shared, so both subgroups walk as many tiles as subgroup 0; the
 // tiles past subgroup 1's own count load in bounds (the last tile) and
 // neither compute nor store.
-// f(integral_constant<e>) for the runtime value e in [E, D)
-template <int E, int D, typename F>
-__device__ __forceinline__ void drain_case(uint32_t e, F &&f) {
-  if constexpr (E < D) {
-    if (e == (uint32_t)E)
-      f(std::integral_constant<int, E>{});
-    else
-      drain_case<E + 1, D>(e, f);
-  }
-}
-
 template <int MMAX, int NW, int DEPTH, int UA, int SG = 1, int LATE = 0>
 __global__ __launch_bounds__(64 * NW * SG) void q2_0_pairs_kernel(const uint16_t *__restrict__ A,
                                                                   const uint8_t *__restrict__ B,
