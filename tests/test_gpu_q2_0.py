@@ -150,11 +150,12 @@ def test_ffn_shapes(oracle_mod, N, K):
 @pytest.mark.parametrize("N,K,M", [(37, 12288, 8), (200, 12288, 7), (1, 12288, 8), (333, 17408, 6), (2049, 10240, 8),
                                    (9216, 17408, 8), (10496, 17408, 5)])
 def test_large_k_batched_rows(oracle_mod, N, K, M):
-    """Activations too large for LDS (the per-phase kernel with super-tiles of
-    up to four 8-row tiles over an even row split; N = 9216 and 10496 on 256
-    CUs give 36 and 41 rows per workgroup, two super-tiles): ragged N, every
-    row bit-identical to its own M=1 launch (the resident-activation kernel)
-    and within tolerance of the oracle on a column sample."""
+    """Activations too large for LDS: the segmented kernel where a
+    workgroup's share of the rows fits in four 8-row tiles, else the
+    per-phase kernel with super-tiles of up to four tiles (N = 9216 and 10496
+    on 256 CUs give 36 and 41 rows per workgroup, two super-tiles): ragged N,
+    every row bit-identical to its own M=1 launch (the resident-activation
+    kernel) and within tolerance of the oracle on a column sample."""
     A, codes, d, packed = _case(31, N, K, M, salt=N + K)
     Bd = dev_u8(packed)
     got = q2_0_gpu(A, Bd, N, K)
@@ -172,8 +173,9 @@ def test_two_to_four_rows_every_staging_tier(oracle_mod, N, K, M):
     request follows the staging barrier above (and at K = 17408, N = 2052,
     where two copies of the activations do not fit in LDS), with the staging
     chunks per thread that cover A (M = 3 at K = 5120 takes 4, M = 4 takes 5,
-    M = 2 at K = 17408 takes 9, M = 3 and 4 there two rounds of 10); ragged N
-    (4100 and 2052 end in a partial tile).  Every row bit-identical to its own
+    M = 2 at K = 17408 takes 9); M = 3 and 4 at N = 5120, K = 17408 (104 and
+    139 KB of activations over three tiles per workgroup) run the segmented
+    kernel; ragged N (4100 and 2052 end in a partial tile).  Every row bit-identical to its own
     M=1 launch, a canary row past M untouched, a column sample within
     tolerance of the oracle."""
     A, codes, d, packed = _case(41, N, K, M, salt=N * 7 + K + M)
@@ -211,6 +213,33 @@ def test_five_to_eight_rows_tile_counts(oracle_mod, N, K, M):
     check_parity(got[:, cols], oracle_mod.q2_0_gemv(A, codes[cols], d[cols]), f"q2_0 {N}x{K} M={M}")
 
 
+@pytest.mark.parametrize("N,K,M", [(3, 20480, 8), (17, 17408, 8), (2049, 10240, 8), (4100, 17408, 5),
+                                   (5120, 17408, 3), (4096, 12288, 4), (5120, 6144, 8), (5120, 8192, 6),
+                                   (8192, 20480, 7)])
+def test_segmented_kernel_tiles_and_segments(oracle_mod, N, K, M):
+    """The segmented kernel over every tile count per workgroup (on 256 CUs:
+    N = 3 and 17, one tile holding 3 and 6 rows; 2049, two; 4100, three or
+    two in one launch; 8192, four), full and partial last segments (K = 17408:
+    four segments of 16 pairs and one of 4; 10240 and 6144: two and one, or
+    one and one, of 8; 20480 and 8192: full ones only; 32-pair segments for up
+    to four rows, K = 17408 M = 3: two and one of 4, K = 12288 M = 4: one and
+    one of 16), the 4-, 6- and 8-row instances, and both ways in:
+    activations too large for LDS, and resident ones of 96 KB or more over two
+    or three tiles (4096 x 12288 M = 4, 5120 x 6144 M = 8, 5120 x 8192 M = 6).
+    Every row bit-identical to its own M=1 launch (the resident-activation
+    kernel), a canary row past M untouched, all columns (or a sample holding
+    the last one) within tolerance of the oracle."""
+    A, codes, d, packed = _case(59, N, K, M, salt=N * 5 + K + M)
+    Bd = dev_u8(packed)
+    got = q2_0_gpu(A, Bd, N, K, extra_rows=1)
+    assert np.all(got[M] == CANARY)
+    got = got[:M]
+    for m in range(M):
+        assert np.array_equal(got[m:m + 1], q2_0_gpu(A[m:m + 1], Bd, N, K, single=True)), m
+    cols = np.arange(N) if N <= 400 else np.union1d(gen.rng(953, N, K).choice(N, 256, replace=False), [N - 1])
+    check_parity(got[:, cols], oracle_mod.q2_0_gemv(A, codes[cols], d[cols]), f"q2_0 {N}x{K} M={M}")
+
+
 _TIER_CHILD = r"""
 import sys
 import numpy as np
@@ -233,7 +262,7 @@ def test_exact_row_tiers_equal_base_tier_bits(tmp_path):
     onto the 8-row tier (page "w4a16_gemv_tiers.rs", "Kill switch"); run in a
     child process with the switch set, every output is bit-identical to this
     process's exact-tier launch, over the resident-activation kernel, the
-    per-phase kernel (K = 17408) and the two-subgroup path (N = 17400)."""
+    segmented kernel (K = 17408) and the two-subgroup path (N = 17400)."""
     import subprocess
     import sys
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))

@@ -370,6 +370,240 @@ __global__ __launch_bounds__(kThreads) void q2_0_phase_kernel(const uint16_t *__
 }
 
 // ---------------------------------------------------------------------------
+// Segmented kernel: for large activations (too large for LDS, or large
+// enough that staging them all before the first unit costs more than
+// staging them in pieces), with a workgroup's share of the rows in at most
+// TMAX tiles.  The pairs kernel's units, seeds, chains and reduction order,
+// so the same bits.
+//   * One workgroup per CU owns rows [r0, r1) (an even split of N) as T <= TMAX
+//     8-row tiles; rows past r1 re-read row r1 - 1 and are never stored.
+//   * K is walked in segments of SP block pairs.  A segment of every
+//     activation row is staged in LDS once per workgroup (the pairs kernel's
+//     permuted order) into one of two buffers: the next segment's loads are
+//     in flight while the current one is used, one barrier per segment.
+//   * Wave w owns pairs w, w + 8, ...; SP is a multiple of 8, so it meets them
+//     in ascending order, segment after segment.  A unit is one pair for all
+//     T tiles: the lane's activations are read from LDS and the seed chain is
+//     run once, then feed TMAX chains of four MFMA, one per tile, each tile
+//     with its own accumulator.
+//   * Weights go straight from memory to the lanes (the pairs kernel's 12-byte
+//     windows), one segment's units ahead: a wave computes from its ring
+//     registers in place and requests the unit DEPTH ahead into them.  A
+//     request past the wave's last pair, or for a tile past the workgroup's
+//     rows, lies outside the buffer's range and fetches nothing (such a tile
+//     computes on zeros and is never stored).
+//   * After the last segment the 16 partial sums of each output are added in
+//     LDS in the pairs kernel's order and rows m < M are stored.
+// Measured on MI355X (graph-replayed, cold weights) against the per-phase
+// kernel: N = 5120 K = 17408 M = 8 14.7 -> 11.9 us, M = 5 13.3 -> 10.8; and
+// against the pairs kernel with the activations resident: K = 17408 M = 4
+// 12.7 -> 11.8, M = 3 12.5 -> 11.5, K = 8192 M = 8 9.1 -> 7.8, M = 6 9.1 ->
+// 7.5, K = 6144 M = 8 7.4 -> 6.7, K = 12288 M = 4 10.3 -> 9.9.  What did not
+// pay: requesting weights and activations two segments ahead (M = 8 11.9 ->
+// 13.6 us: more requests in flight, and the compute units' address path is
+// already busy most of the kernel with the 278 KB of activations each CU
+// stages), and three buffers with a per-wave arrival counter in LDS instead
+// of the barrier, so waves may run a segment apart (11.9 -> 12.4).
+// LDS: [zero rows: 256][segment buffer 0][segment buffer 1]; the partial sums
+// reuse it at the end.
+template <int MMAX>
+struct SegShape {
+  static constexpr int kSP = MMAX <= 4 ? 32 : 16;                // block pairs per segment
+  static constexpr int kPitch = kSP * 512 + 16;                  // LDS pitch of an activation row segment
+  static constexpr int kBuf = MMAX * kPitch;                     // one segment buffer
+  static constexpr int kBuf0 = 256;                              // after the zero rows
+  static constexpr int kBytes = kBuf0 + 2 * kBuf;
+  static constexpr int kChunks = MMAX * kSP * 32 / kThreads;     // 16-byte chunks per thread per segment
+  static_assert(kSP % kWaves == 0, "a wave must meet its pairs in ascending order");
+  static_assert(MMAX * kSP * 32 % kThreads == 0, "whole staging rounds");
+  static_assert(kBytes <= (int)kLdsMax, "two segment buffers must fit in LDS");
+};
+// Buffer offset of a request with nothing to fetch: beyond every weight and
+// activation buffer the kernel accepts (under 2^31 bytes), and below 2^32
+// after adding a pair offset.
+constexpr uint32_t kPastEnd = 0x80000000u;
+
+template <int MMAX, int TMAX, int DEPTH>
+__global__ __launch_bounds__(kThreads) void q2_0_segs_kernel(const uint16_t *__restrict__ A,
+                                                             const uint8_t *__restrict__ B,
+                                                             uint16_t *__restrict__ C, uint32_t N, uint32_t K,
+                                                             uint32_t M) {
+  using G = SegShape<MMAX>;
+  constexpr uint32_t kSP = G::kSP, kUps = kSP / kWaves;  // a wave's units per full segment
+  constexpr int NF = MMAX < 4 ? MMAX : 4;                // accumulator rows that can hold outputs
+  static_assert(DEPTH == (int)kUps, "the ring holds one segment's units");
+  static_assert(TMAX * kSlots8 * 2 * MMAX * kRows * 4 <= G::kBytes, "the partial sums reuse the buffers");
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const uint32_t tid = threadIdx.x;
+  const uint32_t lane = tid & 63u;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t i = lane & 15u, g = lane >> 4;
+  const uint32_t h = i >> 3, rw = i & 7u;  // MFMA column i = (block half h, weight row rw)
+  const uint32_t nb = K >> 7, npairs = nb >> 1;
+  const uint32_t nseg = (npairs + kSP - 1u) / kSP;
+
+  // Staging: chunk c = u * 512 + tid of a segment is activation row
+  // c / (32 SP), 16-byte column c % (32 SP); segment s adds s * 512 SP bytes
+  // (a scalar offset).  Rows m >= M fetch nothing (their zeros land in buffer
+  // rows no lane reads); columns past K in the last segment fetch the next
+  // row's start or nothing, and no lane reads them either.  The first
+  // segment's loads go out before any other set-up.
+  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(A), (short)0, (int)(M * K * 2u), 0x00020000);
+  u32x4_t av[G::kChunks];
+  uint32_t a_src[G::kChunks], a_dst[G::kChunks];
+#pragma unroll
+  for (int u = 0; u < G::kChunks; ++u) {
+    const uint32_t c = (uint32_t)u * kThreads + tid;
+    const uint32_t m = c / (32u * kSP), col = c % (32u * kSP);
+    a_src[u] = m < M ? m * 2u * K + 16u * col : kPastEnd;
+    a_dst[u] = (uint32_t)G::kBuf0 + m * (uint32_t)G::kPitch + 16u * col;
+  }
+  auto stage_load = [&](uint32_t s) {
+#pragma unroll
+    for (int u = 0; u < G::kChunks; ++u)
+      av[u] = __builtin_amdgcn_raw_buffer_load_b128(arsrc, a_src[u], s * kSP * 512u, 0);
+  };
+  auto stage_store = [&](uint32_t s) {
+    const uint32_t boff = (s & 1u) * (uint32_t)G::kBuf;
+#pragma unroll
+    for (int u = 0; u < G::kChunks; ++u) *reinterpret_cast<u32x4_t *>(lds + a_dst[u] + boff) = permute_acts(av[u]);
+  };
+  stage_load(0u);
+
+  uint32_t r0, r1;
+  even_rows(N, blockIdx.x, gridDim.x, r0, r1);
+  const uint32_t T = (r1 - r0 + (uint32_t)kRows - 1u) / (uint32_t)kRows;  // <= TMAX (checked by the launcher)
+  const uint32_t rb = nb * kBlockBytes;
+  const uint32_t nq = npairs > wave ? (npairs - wave + kWaves - 1u) / kWaves : 0u;  // the wave's pairs
+  const __amdgpu_buffer_rsrc_t wrsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(B), (short)0, (int)(N * rb), 0x00020000);
+  uint32_t voff[TMAX];
+#pragma unroll
+  for (int t = 0; t < TMAX; ++t) {
+    const uint32_t row = min(r0 + (uint32_t)kRows * (uint32_t)t + rw, r1 - 1u);
+    voff[t] = (uint32_t)t < T ? row * rb + 32u * h + 8u * g : kPastEnd;
+  }
+
+  // unit q of this wave is pair wave + 8 q, for every tile
+  struct SegRegs {
+    u32x3_t w[TMAX];
+  };
+  auto issue = [&](uint32_t q) {
+    const bool live = q < nq;
+    const uint32_t soff = 68u * (wave + kWaves * q);
+    SegRegs r;
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) r.w[t] = __builtin_amdgcn_raw_buffer_load_b96(wrsrc, live ? voff[t] : kPastEnd, soff, 0);
+    return r;
+  };
+
+  SegRegs ring[DEPTH];
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) ring[d] = issue((uint32_t)d);
+  if (tid < 16u) {  // zero region standing in for activation rows m >= M
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4_t *>(lds + 16u * tid) = z;
+  }
+  stage_store(0u);
+  __syncthreads();
+  stage_load(min(1u, nseg - 1u));  // (a single segment re-reads itself, stored nowhere)
+
+  const bool a_ok = rw < M;
+  const uint32_t a_lane = a_ok ? (uint32_t)G::kBuf0 + rw * G::kPitch + h * 256u + 64u * g : 64u * g;
+  const uint32_t a_buf = a_ok ? (uint32_t)G::kBuf : 0u;  // per buffer
+  const uint32_t a_stride = a_ok ? 512u : 0u;            // per pair
+  const uint32_t sel = h ? 0x07060504u : 0x05040302u;    // the 8 code bytes at byte 2 (h = 0) or 4 (h = 1)
+  const bool lane_out = (g >> 1) == h;
+
+  f32x4_t acc[TMAX];
+#pragma unroll
+  for (int t = 0; t < TMAX; ++t) acc[t] = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
+  // every tile is computed (a tile past the workgroup's rows sees zero
+  // weights and is never stored), so the T chains interleave
+  auto unit = [&](const SegRegs &r, uint32_t q, uint32_t s) {
+    const uint32_t pl = wave + kWaves * q - s * kSP;  // pair within the segment
+    const uint8_t *act = lds + a_lane + (s & 1u) * a_buf + a_stride * pl;
+    bf16x8_t a[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = *reinterpret_cast<const bf16x8_t *>(act + 16 * j);
+    const f32x4_t seed = neg_sum_chain(a);
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      const u32x3_t w = r.w[t];
+      const uint32_t w0 = __builtin_amdgcn_perm(w.y, w.x, sel);
+      const uint32_t w1 = __builtin_amdgcn_perm(w.z, w.y, sel);
+      const uint32_t own_d = h ? (w.x >> 16) : (w.x & 0xFFFFu);  // meaningful on lanes g = 0
+      const uint32_t dbits = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(i << 2), (int)own_d);
+      const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)dbits);
+      bf16x8_t b0, b1, b2, b3;
+      decode_word(w0, b0, b1);
+      decode_word(w1, b2, b3);
+      f32x4_t x = seed;
+      x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b0, x, 0, 0, 0);
+      x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], b1, x, 0, 0, 0);
+      x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2], b2, x, 0, 0, 0);
+      x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[3], b3, x, 0, 0, 0);
+#pragma unroll
+      for (int rr = 0; rr < NF; ++rr) acc[t][rr] = __builtin_fmaf((float)d, x[rr], acc[t][rr]);
+    }
+  };
+
+  // Every segment but the last is full (each wave owns kUps of its pairs
+  // there) and runs as straight-line code: compute from the ring registers
+  // in place and request the unit DEPTH ahead into them (past the wave's last
+  // pair: a request that fetches nothing).  The last segment's units were
+  // all requested by then.
+  const uint32_t nlast = nseg - 1u;
+  uint32_t q = 0;
+  for (uint32_t s = 0; s < nlast; ++s) {
+#pragma unroll
+    for (int u = 0; u < DEPTH; ++u) {
+      unit(ring[u], q, s);
+      ring[u] = issue(q + DEPTH);
+      ++q;
+    }
+    stage_store(s + 1u);  // that buffer was last read in segment s - 1, before the previous barrier
+    __syncthreads();
+    stage_load(min(s + 2u, nlast));  // (the last segment re-read at the end, stored nowhere)
+  }
+#pragma unroll
+  for (int u = 0; u < DEPTH; ++u) {
+    if (q < nq) unit(ring[u], q, nlast);
+    ++q;
+  }
+
+  // the 16 partial sums of each output, added in slot and half order
+  __syncthreads();  // every wave is done with the segment buffers
+  float *part = reinterpret_cast<float *>(lds);  // [tile][slot][half][m][r]
+  if (lane_out) {
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      if ((uint32_t)t < T) {
+#pragma unroll
+        for (int rr = 0; rr < NF; ++rr) {
+          const uint32_t m = 4u * (g & 1u) + rr;
+          if (m < M) part[((((uint32_t)t * kSlots8 + wave) * 2u + h) * MMAX + m) * kRows + rw] = acc[t][rr];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t per = M * (uint32_t)kRows;
+  if (tid < T * per) {
+    const uint32_t t = tid / per, lt = tid - t * per;
+    const uint32_t m = lt >> 3, col = lt & 7u;
+    const uint32_t n = r0 + (uint32_t)kRows * t + col;
+    if (n < r1) {
+      const float *pp = part + ((t * kSlots8 * 2u) * MMAX + m) * kRows + col;
+      float v = pp[0];
+      for (uint32_t k = 1; k < 2u * kSlots8; ++k) v = v + pp[k * MMAX * kRows];
+      store_out(C + (size_t)m * N + n, f32_to_bf16_rne(v));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Resident-activation kernel (the usual case): per-wave block pairs.
 // ---------------------------------------------------------------------------
 // LDS: [zero rows: 256][partial tiles, per subgroup: 2 x 8 slots x 2 x MMAX x 8 floats]
@@ -743,13 +977,25 @@ hipError_t launch_phase_tpp(uint32_t grid, hipStream_t stream, const uint16_t *a
   return hipGetLastError();
 }
 
-// One workgroup per CU (one needs up to 135 KB of LDS at 8 rows), the rows
-// split evenly; super-tiles as wide as the share of rows needs, up to 4
-// tiles (32 rows), so every CU streams the same bytes and fetches the
-// activations once per super-tile.
-template <int MMAX>
-hipError_t launch_phase(const uint16_t *a, const uint8_t *b, uint16_t *c, uint32_t N, uint32_t K, uint32_t M,
-                        hipStream_t stream) {
+template <int MMAX, int TMAX>
+hipError_t launch_segs_t(uint32_t grid, hipStream_t stream, const uint16_t *a, const uint8_t *b, uint16_t *c,
+                         uint32_t N, uint32_t K, uint32_t M) {
+  constexpr auto kern = q2_0_segs_kernel<MMAX, TMAX, SegShape<MMAX>::kSP / kWaves>;
+  constexpr size_t lds = SegShape<MMAX>::kBytes;
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, stream, a, b, c, N, K, M);
+  return hipGetLastError();
+}
+
+// The one-workgroup-per-CU grid of the segmented and per-phase kernels: the
+// rows split evenly over min(CUs, tiles) workgroups, and the tiles of one
+// workgroup's share.
+struct EvenGrid {
+  uint32_t grid, rows, tiles;
+};
+inline hipError_t even_grid(uint32_t N, EvenGrid &g) {
   static int cus = 0;
   if (cus == 0) {
     int dev = 0, n = 0;
@@ -759,8 +1005,46 @@ hipError_t launch_phase(const uint16_t *a, const uint8_t *b, uint16_t *c, uint32
     cus = n > 0 ? n : 1;
   }
   const uint32_t ntiles = (N + kRows - 1u) / kRows;
-  const uint32_t grid = ntiles < (uint32_t)cus ? ntiles : (uint32_t)cus;
-  const uint32_t rows = (N + grid - 1u) / grid;
+  g.grid = ntiles < (uint32_t)cus ? ntiles : (uint32_t)cus;
+  g.rows = (N + g.grid - 1u) / g.grid;
+  g.tiles = (g.rows + kRows - 1u) / kRows;
+  return hipSuccess;
+}
+
+// The segmented kernel's limits: a workgroup's rows in at most four tiles,
+// and weights and activations under 2^31 bytes (its requests with nothing to
+// fetch sit past both).  It runs the 4-, 6- and 8-row instances only: one or
+// two rows reach activations of 96 KB at K of 24576 and more, where the
+// pairs and per-phase kernels serve them.
+inline bool segs_fit(const EvenGrid &g, uint32_t N, uint32_t K, uint32_t M) {
+  return g.tiles <= 4u && (uint64_t)N * (K >> 7) * kBlockBytes < (1ull << 31) && (uint64_t)M * K * 2u < (1ull << 31);
+}
+
+template <int MMAX>
+hipError_t launch_segs(const EvenGrid &g, hipStream_t stream, const uint16_t *a, const uint8_t *b, uint16_t *c,
+                       uint32_t N, uint32_t K, uint32_t M) {
+  if (g.tiles <= 1u) return launch_segs_t<MMAX, 1>(g.grid, stream, a, b, c, N, K, M);
+  if (g.tiles <= 2u) return launch_segs_t<MMAX, 2>(g.grid, stream, a, b, c, N, K, M);
+  if (g.tiles <= 3u) return launch_segs_t<MMAX, 3>(g.grid, stream, a, b, c, N, K, M);
+  return launch_segs_t<MMAX, 4>(g.grid, stream, a, b, c, N, K, M);
+}
+
+// Activations too large for LDS: the segmented kernel where a workgroup's
+// rows fit in its tiles, else per phase.  Per phase: one workgroup per CU
+// (one needs up to 135 KB of LDS at 8 rows), the rows split evenly;
+// super-tiles as wide as the share of rows needs, up to 4 tiles (32 rows),
+// so every CU streams the same bytes and fetches the activations once per
+// super-tile.
+template <int MMAX>
+hipError_t launch_phase(const uint16_t *a, const uint8_t *b, uint16_t *c, uint32_t N, uint32_t K, uint32_t M,
+                        hipStream_t stream) {
+  EvenGrid eg;
+  const hipError_t e = even_grid(N, eg);
+  if (e != hipSuccess) return e;
+  if constexpr (MMAX >= 4) {
+    if (segs_fit(eg, N, K, M)) return launch_segs<MMAX>(eg, stream, a, b, c, N, K, M);
+  }
+  const uint32_t grid = eg.grid, rows = eg.rows;
   const uint32_t nsuper = (rows + 4u * kRows - 1u) / (4u * kRows);
   const uint32_t tpp = (rows + kRows * nsuper - 1u) / (kRows * nsuper);
   if (tpp <= 1u) return launch_phase_tpp<MMAX, 1>(grid, stream, a, b, c, N, K, M);
@@ -819,6 +1103,22 @@ hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32
       const uint32_t pt = (M * (K >> 3) + 1023u) / 1024u;
       const uint32_t half = (ntiles + 1u) / 2u;
       return launch_pairs<8, NW, 3, 2, 1>(pt, 1024, lds2, 1, half, stream, a, b, c, N, K, M);
+    }
+  }
+  // Activations of 96 KB or more over two or three tiles per workgroup: the
+  // segmented kernel stages them in pieces behind the first units instead of
+  // all before them (measured in its description; at one tile per workgroup,
+  // N = 2048 K = 17408 M = 4, the pairs kernel stays faster, 7.0 against 7.5
+  // us, at four tiles, N = K = 8192 M = 8, the two tie, and with smaller
+  // activations the pairs kernel is faster: N = 5120 K = 12288 M = 2 8.0
+  // against 8.5, N = K = 8192 M = 4 8.9 against 10.0).
+  if constexpr (MMAX >= 4) {
+    if ((uint64_t)M * K * 2u >= 96u * 1024u) {
+      EvenGrid eg;
+      const hipError_t e = even_grid(N, eg);
+      if (e != hipSuccess) return e;
+      if (eg.tiles >= 2u && eg.tiles <= 3u && segs_fit(eg, N, K, M))
+        return launch_segs<MMAX>(eg, stream, a, b, c, N, K, M);
     }
   }
   const size_t lds = pair_lds_bytes<MMAX>(M, K);
