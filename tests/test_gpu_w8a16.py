@@ -173,12 +173,15 @@ def test_n64_bit_identical_to_contiguous(oracle_mod, N, K, M):
 @pytest.mark.parametrize("N,K,M,pa,pc", [
     (5120, 5120, 1, 0, 0), (5120, 5120, 8, 8, 1), (5120, 5120, 16, 136, 37),
     (130, 1024, 16, 8, 3), (17, 384, 3, 64, 0), (300, 640, 7, 0, 300), (33, 128, 9, 1024, 5),
+    (300, 17408, 7, 72, 5), (2000, 16512, 12, 8, 0),
 ])
 def test_strided_rows_equal_contiguous_and_padding_untouched(oracle_mod, N, K, M, pa, pc):
     """A and C as row slices of wider buffers (page "w8a16_gemm_m16.rs",
     w8a16_gemm_m16_strided): each output row equals the contiguous call's, the
     activation padding (filled with NaN bit patterns) is never read into a
-    sum, and C's padding columns and rows >= M keep their canary."""
+    sum, and C's padding columns and rows >= M keep their canary.  The last
+    two shapes run the segmented kernel, whose last K-segment copies part of
+    each row's padding into LDS (K = 16512 ends in a partial segment)."""
     from weight_quantized_decode_block_amd import wqd
     A, W, S = _case(22, N, K, M, salt=N + 5 * K)
     Wd, Sd = dev_u8(W), dev_f32(S)
