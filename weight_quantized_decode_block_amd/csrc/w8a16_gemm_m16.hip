@@ -643,11 +643,11 @@ __global__ __launch_bounds__(kThreads) void w8a16_regs_kernel(const uint16_t *__
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(W), (short)0, (int)(N * K), 0x00020000);
   const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float *>(S), (short)0, (int)(((N + 127u) >> 7) * nb * 4u), 0x00020000);
-  // block u of this wave in tile t (t = ntile: nothing)
+  // block u of this wave in tile t (t = ntile, or u past the wave's blocks: nothing)
   auto issue = [&](uint32_t t, uint32_t u) __attribute__((always_inline)) {
     const uint32_t b = min(wave + kWaves * u, nb - 1u);
     const uint32_t row = r0 + 16u * t + i;
-    const bool ok = t < ntile && row < r1;
+    const bool ok = t < ntile && row < r1 && u < upw;
     const uint32_t voff = ok ? row * K + 32u * g : kPastEnd;
     const uint32_t srow = (ok ? row : r0) >> 7;
     UnitRegs r;
@@ -669,11 +669,15 @@ __global__ __launch_bounds__(kThreads) void w8a16_regs_kernel(const uint16_t *__
   float *part = reinterpret_cast<float *>(lds + L::kPart);
   for (uint32_t t = 0; t < ntile; ++t) {
     f32x4_t outer = {0.0f, 0.0f, 0.0f, 0.0f};
+    // compute from the ring registers in place, then request the next
+    // tile's block into them (no request behind a branch, no register copy
+    // that would wait for a load in flight; measured on MI355X against a copy
+    // taken before the request, N = K = 5120 M = 16 11.77 -> 11.42 us, M = 9
+    // 10.30 -> 9.61, N = 17408 M = 16 24.4 -> 22.7)
     unroll<0, NBW>([&](auto uu) __attribute__((always_inline)) {
       constexpr int u = decltype(uu)::value;
       if ((uint32_t)u < upw) {
-        const UnitRegs r = ring[u];
-        ring[u] = issue(t + 1u, (uint32_t)u);
+        const UnitRegs &r = ring[u];
         f32x4_t x = {0.0f, 0.0f, 0.0f, 0.0f};
         x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][0], weights8(r.w0.x, r.w0.y), x, 0, 0, 0);
         x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][1], weights8(r.w0.z, r.w0.w), x, 0, 0, 0);
@@ -682,6 +686,7 @@ __global__ __launch_bounds__(kThreads) void w8a16_regs_kernel(const uint16_t *__
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) outer[rr] = __fadd_rn(outer[rr], __fmul_rn(r.s, x[rr]));
       }
+      ring[u] = issue(t + 1u, (uint32_t)u);
     });
     // the 8 waves' partial tiles, added in wave order (tile parity alternates
     // the buffer, so one barrier per tile suffices)
