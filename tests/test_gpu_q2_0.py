@@ -148,14 +148,16 @@ def test_ffn_shapes(oracle_mod, N, K):
 
 
 @pytest.mark.parametrize("N,K,M", [(37, 12288, 8), (200, 12288, 7), (1, 12288, 8), (333, 17408, 6), (2049, 10240, 8),
-                                   (9216, 17408, 8), (10496, 17408, 5)])
+                                   (9216, 17408, 8), (10496, 17408, 5), (12304, 12288, 8), (8200, 20480, 4)])
 def test_large_k_batched_rows(oracle_mod, N, K, M):
     """Activations too large for LDS: the segmented kernel where a
-    workgroup's share of the rows fits in four 8-row tiles, else the
-    per-phase kernel with super-tiles of up to four tiles (N = 9216 and 10496
-    on 256 CUs give 36 and 41 rows per workgroup, two super-tiles): ragged N,
-    every row bit-identical to its own M=1 launch (the resident-activation
-    kernel) and within tolerance of the oracle on a column sample."""
+    workgroup's share of the rows fits in six 8-row tiles (N = 9216 and 10496
+    on 256 CUs give 36 and 41 rows per workgroup, five and six tiles), else
+    the per-phase kernel with super-tiles of up to four tiles (N = 12304: 49
+    rows, seven tiles, two super-tiles; N = 8200 M = 4: 33 rows, five tiles,
+    beyond the 4-row segmented instance): ragged N, every row bit-identical to
+    its own M=1 launch (the resident-activation kernel) and within tolerance
+    of the oracle on a column sample."""
     A, codes, d, packed = _case(31, N, K, M, salt=N + K)
     Bd = dev_u8(packed)
     got = q2_0_gpu(A, Bd, N, K)

@@ -373,8 +373,8 @@ __global__ __launch_bounds__(kThreads) void q2_0_phase_kernel(const uint16_t *__
 // Segmented kernel: for large activations (too large for LDS, or large
 // enough that staging them all before the first unit costs more than
 // staging them in pieces), with a workgroup's share of the rows in at most
-// TMAX tiles.  The pairs kernel's units, seeds, chains and reduction order,
-// so the same bits.
+// TMAX tiles (up to six).  The pairs kernel's units, seeds, chains and
+// reduction order, so the same bits.
 //   * One workgroup per CU owns rows [r0, r1) (an even split of N) as T <= TMAX
 //     8-row tiles; rows past r1 re-read row r1 - 1 and are never stored.
 //   * K is walked in segments of SP block pairs.  A segment of every
@@ -1011,13 +1011,18 @@ inline hipError_t even_grid(uint32_t N, EvenGrid &g) {
   return hipSuccess;
 }
 
-// The segmented kernel's limits: a workgroup's rows in at most four tiles,
-// and weights and activations under 2^31 bytes (its requests with nothing to
-// fetch sit past both).  It runs the 4-, 6- and 8-row instances only: one or
-// two rows reach activations of 96 KB at K of 24576 and more, where the
-// pairs and per-phase kernels serve them.
+// The segmented kernel's limits: a workgroup's rows in at most six tiles
+// (four for the 4-row instance, whose deeper ring would not fit in
+// registers beyond that), and weights and activations under 2^31 bytes (its
+// requests with nothing to fetch sit past both).  It runs the 4-, 6- and
+// 8-row instances only: one or two rows reach activations of 96 KB at K of
+// 24576 and more, where the pairs and per-phase kernels serve them.
+// Measured on MI355X against the per-phase kernel at five and six tiles:
+// N = 9216 K = 17408 M = 8 25.8 -> 17.1 us, N = 10496 M = 5 23.3 -> 18.2,
+// N = 12288 M = 8 27.2 -> 20.1.
+template <int MMAX>
 inline bool segs_fit(const EvenGrid &g, uint32_t N, uint32_t K, uint32_t M) {
-  return g.tiles <= 4u && (uint64_t)N * (K >> 7) * kBlockBytes < (1ull << 31) && (uint64_t)M * K * 2u < (1ull << 31);
+  return g.tiles <= (MMAX <= 4 ? 4u : 6u) && (uint64_t)N * (K >> 7) * kBlockBytes < (1ull << 31) && (uint64_t)M * K * 2u < (1ull << 31);
 }
 
 template <int MMAX>
@@ -1026,7 +1031,13 @@ hipError_t launch_segs(const EvenGrid &g, hipStream_t stream, const uint16_t *a,
   if (g.tiles <= 1u) return launch_segs_t<MMAX, 1>(g.grid, stream, a, b, c, N, K, M);
   if (g.tiles <= 2u) return launch_segs_t<MMAX, 2>(g.grid, stream, a, b, c, N, K, M);
   if (g.tiles <= 3u) return launch_segs_t<MMAX, 3>(g.grid, stream, a, b, c, N, K, M);
-  return launch_segs_t<MMAX, 4>(g.grid, stream, a, b, c, N, K, M);
+  if constexpr (MMAX <= 4) {
+    return launch_segs_t<MMAX, 4>(g.grid, stream, a, b, c, N, K, M);
+  } else {
+    if (g.tiles <= 4u) return launch_segs_t<MMAX, 4>(g.grid, stream, a, b, c, N, K, M);
+    if (g.tiles <= 5u) return launch_segs_t<MMAX, 5>(g.grid, stream, a, b, c, N, K, M);
+    return launch_segs_t<MMAX, 6>(g.grid, stream, a, b, c, N, K, M);
+  }
 }
 
 // Activations too large for LDS: the segmented kernel where a workgroup's
@@ -1042,7 +1053,7 @@ hipError_t launch_phase(const uint16_t *a, const uint8_t *b, uint16_t *c, uint32
   const hipError_t e = even_grid(N, eg);
   if (e != hipSuccess) return e;
   if constexpr (MMAX >= 4) {
-    if (segs_fit(eg, N, K, M)) return launch_segs<MMAX>(eg, stream, a, b, c, N, K, M);
+    if (segs_fit<MMAX>(eg, N, K, M)) return launch_segs<MMAX>(eg, stream, a, b, c, N, K, M);
   }
   const uint32_t grid = eg.grid, rows = eg.rows;
   const uint32_t nsuper = (rows + 4u * kRows - 1u) / (4u * kRows);
@@ -1117,7 +1128,7 @@ hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32
       EvenGrid eg;
       const hipError_t e = even_grid(N, eg);
       if (e != hipSuccess) return e;
-      if (eg.tiles >= 2u && eg.tiles <= 3u && segs_fit(eg, N, K, M))
+      if (eg.tiles >= 2u && eg.tiles <= 3u && segs_fit<MMAX>(eg, N, K, M))
         return launch_segs<MMAX>(eg, stream, a, b, c, N, K, M);
     }
   }
