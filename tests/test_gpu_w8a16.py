@@ -81,6 +81,28 @@ def test_every_staging_tier_rows_bit_identical(oracle_mod, N, K, M):
     check_parity(got[:, cols], ref, f"w8a16 {N}x{K} M={M}")
 
 
+@pytest.mark.parametrize("N,K,M", [(300, 640, 13), (4100, 5120, 16), (20480, 2048, 9), (20736, 1024, 12),
+                                   (20744, 5120, 16)])
+def test_nine_to_sixteen_rows_kernels(oracle_mod, N, K, M):
+    """Nine to sixteen rows: the segmented kernel over one, two and five
+    16-row tiles per workgroup (on 256 CUs: N = 300, 4100, 20480), and the
+    registers kernel where a workgroup's rows need more than five tiles
+    (N = 20736, K = 1024: 81 rows, six tiles; N = 20744, K = 5120: five
+    blocks per wave).  Every row bit-identical to its own M=1 call (the units
+    kernel), rows past M untouched, a column sample (holding the last one)
+    within tolerance of the oracle."""
+    A, W, S = _case(27, N, K, M, salt=N + 7 * K)
+    Wd, Sd = dev_u8(W), dev_f32(S)
+    got = w8a16_gpu(A, Wd, Sd, N, K, c_rows=16)
+    assert np.all(got[M:] == CANARY)
+    got = got[:M]
+    for m in range(M):
+        assert np.array_equal(w8a16_gpu(A[m:m + 1], Wd, Sd, N, K), got[m:m + 1]), f"row {m}"
+    cols = np.arange(N) if N <= 400 else np.union1d(gen.rng(911, N, K).choice(N, 256, replace=False), [N - 1])
+    ref = np.concatenate([oracle_mod.w8a16_gemm(A, W[c:c + 1], S[c // 128:c // 128 + 1]) for c in cols], axis=1)
+    check_parity(got[:, cols], ref, f"w8a16 {N}x{K} M={M}")
+
+
 @pytest.mark.parametrize("N,K,M", [(130, 1024, 16), (16, 128, 1), (300, 640, 7)])
 def test_exact_integer_regime_bit_identical(oracle_mod, N, K, M):
     A = gen.exact_activations(N + M + 1, M, K)

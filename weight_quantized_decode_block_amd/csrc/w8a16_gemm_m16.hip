@@ -989,24 +989,20 @@ hipError_t launch_w8a16_m16(const void *A, const void *W, const float *S, void *
   // every kernel gives the same bits; the choice is by speed and by what fits
   const bool bounded = (uint64_t)N * K < (1ull << 31);
   const uint32_t nbw = ((K >> 7) + kWaves - 1u) / kWaves;  // blocks per wave and tile
-  // 9..16 rows with up to 5 blocks per wave (K <= 5120): activations in
-  // registers (measured on MI355X at N = K = 5120, M = 16: 12.7 us against
-  // 16.2 us per phase).  Up to 8 rows the LDS copy is cheaper: each wave
-  // would otherwise fetch its own copy of the activations.
-  if (bounded && M > 8 && nbw <= 5u) {
-    if (nbw <= 1u) return launch_regs<1>(A, W, S, C, M, N, K, lda, ldc, band, stream);
-    if (nbw <= 2u) return launch_regs<2>(A, W, S, C, M, N, K, lda, ldc, band, stream);
-    if (nbw <= 4u) return launch_regs<4>(A, W, S, C, M, N, K, lda, ldc, band, stream);
-    return launch_regs<5>(A, W, S, C, M, N, K, lda, ldc, band, stream);
-  }
+  // Up to 8 rows whose activations fit in LDS: the units kernel (the
+  // segmented kernel is slower there: N = K = 5120 M = 1 9.0 against 7.7 us,
+  // M = 8 9.1 against 8.9).
   if (bounded && M <= 8 && unit_lds_bytes<8>(M, K) <= 160u * 1024u) {
     if (M <= 1) return launch_units_mmax<1>(A, W, S, C, M, N, K, lda, ldc, band, stream);
     if (M <= 2) return launch_units_mmax<2>(A, W, S, C, M, N, K, lda, ldc, band, stream);
     if (M <= 4) return launch_units_mmax<4>(A, W, S, C, M, N, K, lda, ldc, band, stream);
     return launch_units_mmax<8>(A, W, S, C, M, N, K, lda, ldc, band, stream);
   }
-  // activations larger than LDS: segments of K staged once per workgroup for
-  // all its tiles, up to 5 tiles (80 rows) per workgroup
+  // Activations larger than LDS, and 9..16 rows: segments of K staged once
+  // per workgroup for all its tiles, up to 5 tiles (80 rows) per workgroup.
+  // For 9..16 rows it beats keeping the activations in registers (measured on
+  // MI355X: N = K = 5120 M = 16 11.40 -> 10.08 us, M = 12 10.35 -> 9.97,
+  // N = 17408 M = 16 22.7 -> 21.9, N = K = 4096 M = 16 8.11 -> 7.82).
   if (bounded && (uint64_t)(M - 1u) * lda + K < (1ull << 30)) {  // (its activation buffer range fits an int)
     SegGrid sg;
     const hipError_t e = seg_grid(N, band, sg);
@@ -1015,6 +1011,15 @@ hipError_t launch_w8a16_m16(const void *A, const void *W, const float *S, void *
       if (M <= 8) return launch_segs<8>(sg, stream, A, W, S, C, M, N, K, lda, ldc, band);
       return launch_segs<16>(sg, stream, A, W, S, C, M, N, K, lda, ldc, band);
     }
+  }
+  // 9..16 rows over more than five tiles per workgroup with up to 5 blocks per
+  // wave (K <= 5120): activations in registers (N = K = 5120, M = 16: 12.7 us
+  // against 16.2 us per phase, when it served that shape).
+  if (bounded && M > 8 && nbw <= 5u) {
+    if (nbw <= 1u) return launch_regs<1>(A, W, S, C, M, N, K, lda, ldc, band, stream);
+    if (nbw <= 2u) return launch_regs<2>(A, W, S, C, M, N, K, lda, ldc, band, stream);
+    if (nbw <= 4u) return launch_regs<4>(A, W, S, C, M, N, K, lda, ldc, band, stream);
+    return launch_regs<5>(A, W, S, C, M, N, K, lda, ldc, band, stream);
   }
   if (M <= 4) return launch_slots<slots_for(4)>(A, W, S, C, M, N, K, lda, ldc, band, stream);
   if (M <= 8) return launch_slots<slots_for(8)>(A, W, S, C, M, N, K, lda, ldc, band, stream);
