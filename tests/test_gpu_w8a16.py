@@ -58,7 +58,7 @@ def test_rows_bit_identical_across_m(oracle_mod):
 
 
 @pytest.mark.parametrize("N,K,M", [(5120, 5120, 2), (5120, 5120, 3), (5120, 5120, 4), (5120, 17408, 1),
-                                   (5120, 17408, 3), (1000, 5120, 4), (520, 4096, 1), (264, 4096, 3),
+                                   (1000, 17408, 3), (1000, 5120, 4), (520, 4096, 1), (264, 4096, 3),
                                    (136, 4096, 5), (136, 4096, 6), (72, 4096, 7), (72, 4096, 8), (1040, 12288, 3),
                                    (200, 8192, 5), (264, 6144, 8)])
 def test_every_staging_tier_rows_bit_identical(oracle_mod, N, K, M):
@@ -66,7 +66,9 @@ def test_every_staging_tier_rows_bit_identical(oracle_mod, N, K, M):
     per thread that cover it in one round, M * K / 4096 of them: 1 to 10 here
     (K = 4096 at M = 1..8, K = 12288 at M = 3, K = 8192 at M = 5; M = 2, 3, 4
     at K = 5120 take 3, 4, 5 with idle slots; M = 1 at K = 17408 takes 5), and
-    two rounds at K = 6144, M = 8: every row bit-identical to its own M=1
+    two rounds at K = 6144, M = 8 and K = 17408, M = 3 (one 16-row tile per
+    workgroup, where these activations stay with this kernel): every row
+    bit-identical to its own M=1
     call, a canary row past M untouched, a column sample within tolerance of
     the oracle."""
     A, W, S = _case(43, N, K, M, salt=N + K + M)
@@ -142,14 +144,17 @@ def test_ffn_shapes(oracle_mod, N, K):
 
 
 @pytest.mark.parametrize("N,K,M", [(5120, 17408, 5), (5120, 17408, 8), (5120, 17408, 12), (1000, 16512, 9),
-                                   (17408, 9216, 10), (300, 17408, 7)])
+                                   (17408, 9216, 10), (300, 17408, 7), (5120, 17408, 3), (8192, 8192, 8),
+                                   (5120, 6144, 8)])
 def test_activations_larger_than_lds(oracle_mod, N, K, M):
-    """Activations larger than LDS (M x K x 2 bytes over 160 KB) are staged in
-    segments of K: every row equals its own M=1 call (which keeps all of A in
-    LDS) bit for bit, the 64-row-band call gives the same bits, and sampled
-    columns are within the parity bar.  Covers K not a multiple of 1024
-    (16512), a workgroup with five 16-row tiles (N = 17408) and one tile
-    (N = 300)."""
+    """Large activations are staged in segments of K: those larger than LDS
+    (M x K x 2 bytes over 160 KB), and resident ones of 96 KB or more (more
+    than 100 KB below five rows) over two or three 16-row tiles per workgroup
+    (N = 5120 K = 17408 M = 3, N = K = 8192 M = 8, N = 5120 K = 6144 M = 8).
+    Every row equals its own M=1 call (which keeps all of A in LDS) bit for
+    bit, the 64-row-band call gives the same bits, and sampled columns are
+    within the parity bar.  Covers K not a multiple of 1024 (16512), a
+    workgroup with five 16-row tiles (N = 17408) and one tile (N = 300)."""
     from weight_quantized_decode_block_amd import wqd
     A, W, S = _case(31, N, K, M, salt=N + K)
     Wd, Sd = dev_u8(W), dev_f32(S)

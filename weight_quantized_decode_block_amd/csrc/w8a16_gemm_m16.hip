@@ -991,7 +991,22 @@ hipError_t launch_w8a16_m16(const void *A, const void *W, const float *S, void *
   const uint32_t nbw = ((K >> 7) + kWaves - 1u) / kWaves;  // blocks per wave and tile
   // Up to 8 rows whose activations fit in LDS: the units kernel (the
   // segmented kernel is slower there: N = K = 5120 M = 1 9.0 against 7.7 us,
-  // M = 8 9.1 against 8.9).
+  // M = 8 9.1 against 8.9, N = 17408 K = 5120 M = 8 20.7 against 19.6),
+  // except for large activations over two or three tiles per workgroup,
+  // which the segmented kernel stages in pieces behind the first units:
+  // 96 KB or more at five to eight rows (N = 5120 K = 6144 M = 8 11.1 -> 10.0
+  // us, K = 8192 M = 6 13.4 -> 12.5, N = K = 8192 M = 8 18.2 -> 17.4), more
+  // than 100 KB at fewer (N = 5120 K = 17408 M = 4 22.5 -> 21.6, M = 3 22.3 ->
+  // 21.5; at 96 KB, K = 12288 M = 4, 17.0 against 17.2, and at one tile per
+  // workgroup, N = 4096, 12.9 against 14.9, the units kernel stays faster).
+  const bool seg_ok = bounded && (uint64_t)(M - 1u) * lda + K < (1ull << 30);  // (its activation range fits an int)
+  const uint64_t a_bytes = (uint64_t)M * K * 2u;
+  if (seg_ok && M <= 8 && ((M >= 5 && a_bytes >= 96u * 1024u) || a_bytes > 100u * 1024u)) {
+    SegGrid sg;
+    const hipError_t e = seg_grid(N, band, sg);
+    if (e != hipSuccess) return e;
+    if (sg.tiles >= 2u && sg.tiles <= 3u) return launch_segs<8>(sg, stream, A, W, S, C, M, N, K, lda, ldc, band);
+  }
   if (bounded && M <= 8 && unit_lds_bytes<8>(M, K) <= 160u * 1024u) {
     if (M <= 1) return launch_units_mmax<1>(A, W, S, C, M, N, K, lda, ldc, band, stream);
     if (M <= 2) return launch_units_mmax<2>(A, W, S, C, M, N, K, lda, ldc, band, stream);
@@ -1003,7 +1018,7 @@ hipError_t launch_w8a16_m16(const void *A, const void *W, const float *S, void *
   // For 9..16 rows it beats keeping the activations in registers (measured on
   // MI355X: N = K = 5120 M = 16 11.40 -> 10.08 us, M = 12 10.35 -> 9.97,
   // N = 17408 M = 16 22.7 -> 21.9, N = K = 4096 M = 16 8.11 -> 7.82).
-  if (bounded && (uint64_t)(M - 1u) * lda + K < (1ull << 30)) {  // (its activation buffer range fits an int)
+  if (seg_ok) {
     SegGrid sg;
     const hipError_t e = seg_grid(N, band, sg);
     if (e != hipSuccess) return e;
