@@ -148,16 +148,18 @@ def test_ffn_shapes(oracle_mod, N, K):
 
 
 @pytest.mark.parametrize("N,K,M", [(37, 12288, 8), (200, 12288, 7), (1, 12288, 8), (333, 17408, 6), (2049, 10240, 8),
-                                   (9216, 17408, 8), (10496, 17408, 5), (12304, 12288, 8), (8200, 20480, 4)])
+                                   (9216, 17408, 8), (10496, 17408, 5), (12304, 12288, 8), (18440, 10240, 8),
+                                   (8200, 20480, 4)])
 def test_large_k_batched_rows(oracle_mod, N, K, M):
     """Activations too large for LDS: the segmented kernel where a
-    workgroup's share of the rows fits in six 8-row tiles (N = 9216 and 10496
-    on 256 CUs give 36 and 41 rows per workgroup, five and six tiles), else
-    the per-phase kernel with super-tiles of up to four tiles (N = 12304: 49
-    rows, seven tiles, two super-tiles; N = 8200 M = 4: 33 rows, five tiles,
-    beyond the 4-row segmented instance): ragged N, every row bit-identical to
-    its own M=1 launch (the resident-activation kernel) and within tolerance
-    of the oracle on a column sample."""
+    workgroup's share of the rows fits in nine 8-row tiles (N = 9216, 10496
+    and 12304 on 256 CUs give 36, 41 and 49 rows per workgroup: five, six and
+    seven tiles, the last with one unit in flight), else the per-phase kernel
+    with super-tiles of up to four tiles (N = 18440: 73 rows, ten tiles, three
+    super-tiles; N = 8200 M = 4: 33 rows, five tiles, beyond the 4-row
+    segmented instance): ragged N, every row bit-identical to its own M=1
+    launch (the resident-activation kernel) and within tolerance of the
+    oracle on a column sample."""
     A, codes, d, packed = _case(31, N, K, M, salt=N + K)
     Bd = dev_u8(packed)
     got = q2_0_gpu(A, Bd, N, K)
@@ -217,11 +219,12 @@ def test_five_to_eight_rows_tile_counts(oracle_mod, N, K, M):
 
 @pytest.mark.parametrize("N,K,M", [(3, 20480, 8), (17, 17408, 8), (2049, 10240, 8), (4100, 17408, 5),
                                    (5120, 17408, 3), (4096, 12288, 4), (5120, 6144, 8), (5120, 8192, 6),
-                                   (8192, 20480, 7)])
+                                   (8192, 20480, 7), (17408, 10240, 8)])
 def test_segmented_kernel_tiles_and_segments(oracle_mod, N, K, M):
     """The segmented kernel over every tile count per workgroup (on 256 CUs:
     N = 3 and 17, one tile holding 3 and 6 rows; 2049, two; 4100, three or
-    two in one launch; 8192, four), full and partial last segments (K = 17408:
+    two in one launch; 8192, four; 17408, nine, whose 576 outputs per
+    workgroup outnumber its threads), full and partial last segments (K = 17408:
     four segments of 16 pairs and one of 4; 10240 and 6144: two and one, or
     one and one, of 8; 20480 and 8192: full ones only; 32-pair segments for up
     to four rows, K = 17408 M = 3: two and one of 4, K = 12288 M = 4: one and

@@ -373,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void q2_0_phase_kernel(const uint16_t *__
 // Segmented kernel: for large activations (too large for LDS, or large
 // enough that staging them all before the first unit costs more than
 // staging them in pieces), with a workgroup's share of the rows in at most
-// TMAX tiles (up to six).  The pairs kernel's units, seeds, chains and
+// TMAX tiles (up to nine).  The pairs kernel's units, seeds, chains and
 // reduction order, so the same bits.
 //   * One workgroup per CU owns rows [r0, r1) (an even split of N) as T <= TMAX
 //     8-row tiles; rows past r1 re-read row r1 - 1 and are never stored.
@@ -431,7 +431,7 @@ __global__ __launch_bounds__(kThreads) void q2_0_segs_kernel(const uint16_t *__r
   using G = SegShape<MMAX>;
   constexpr uint32_t kSP = G::kSP, kUps = kSP / kWaves;  // a wave's units per full segment
   constexpr int NF = MMAX < 4 ? MMAX : 4;                // accumulator rows that can hold outputs
-  static_assert(DEPTH == (int)kUps, "the ring holds one segment's units");
+  static_assert(kUps % DEPTH == 0, "the ring holds whole rounds of a segment's units");
   static_assert(TMAX * kSlots8 * 2 * MMAX * kRows * 4 <= G::kBytes, "the partial sums reuse the buffers");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const uint32_t tid = threadIdx.x;
@@ -558,9 +558,9 @@ __global__ __launch_bounds__(kThreads) void q2_0_segs_kernel(const uint16_t *__r
   uint32_t q = 0;
   for (uint32_t s = 0; s < nlast; ++s) {
 #pragma unroll
-    for (int u = 0; u < DEPTH; ++u) {
-      unit(ring[u], q, s);
-      ring[u] = issue(q + DEPTH);
+    for (int u = 0; u < (int)kUps; ++u) {
+      unit(ring[u % DEPTH], q, s);
+      ring[u % DEPTH] = issue(q + DEPTH);
       ++q;
     }
     stage_store(s + 1u);  // that buffer was last read in segment s - 1, before the previous barrier
@@ -568,8 +568,11 @@ __global__ __launch_bounds__(kThreads) void q2_0_segs_kernel(const uint16_t *__r
     stage_load(min(s + 2u, nlast));  // (the last segment re-read at the end, stored nowhere)
   }
 #pragma unroll
-  for (int u = 0; u < DEPTH; ++u) {
-    if (q < nq) unit(ring[u], q, nlast);
+  for (int u = 0; u < (int)kUps; ++u) {
+    if (q < nq) {
+      unit(ring[u % DEPTH], q, nlast);
+      if (q + DEPTH < nq) ring[u % DEPTH] = issue(q + DEPTH);
+    }
     ++q;
   }
 
@@ -590,8 +593,8 @@ __global__ __launch_bounds__(kThreads) void q2_0_segs_kernel(const uint16_t *__r
   }
   __syncthreads();
   const uint32_t per = M * (uint32_t)kRows;
-  if (tid < T * per) {
-    const uint32_t t = tid / per, lt = tid - t * per;
+  for (uint32_t x = tid; x < T * per; x += kThreads) {  // (more outputs than threads from nine 8-row tiles on)
+    const uint32_t t = x / per, lt = x - t * per;
     const uint32_t m = lt >> 3, col = lt & 7u;
     const uint32_t n = r0 + (uint32_t)kRows * t + col;
     if (n < r1) {
@@ -980,7 +983,7 @@ hipError_t launch_phase_tpp(uint32_t grid, hipStream_t stream, const uint16_t *a
 template <int MMAX, int TMAX>
 hipError_t launch_segs_t(uint32_t grid, hipStream_t stream, const uint16_t *a, const uint8_t *b, uint16_t *c,
                          uint32_t N, uint32_t K, uint32_t M) {
-  constexpr auto kern = q2_0_segs_kernel<MMAX, TMAX, SegShape<MMAX>::kSP / kWaves>;
+  constexpr auto kern = q2_0_segs_kernel<MMAX, TMAX, TMAX >= 7 ? 1 : SegShape<MMAX>::kSP / kWaves>;
   constexpr size_t lds = SegShape<MMAX>::kBytes;
   static const hipError_t attr =
       hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -1011,18 +1014,22 @@ inline hipError_t even_grid(uint32_t N, EvenGrid &g) {
   return hipSuccess;
 }
 
-// The segmented kernel's limits: a workgroup's rows in at most six tiles
+// The segmented kernel's limits: a workgroup's rows in at most nine tiles
 // (four for the 4-row instance, whose deeper ring would not fit in
-// registers beyond that), and weights and activations under 2^31 bytes (its
-// requests with nothing to fetch sit past both).  It runs the 4-, 6- and
-// 8-row instances only: one or two rows reach activations of 96 KB at K of
-// 24576 and more, where the pairs and per-phase kernels serve them.
-// Measured on MI355X against the per-phase kernel at five and six tiles:
-// N = 9216 K = 17408 M = 8 25.8 -> 17.1 us, N = 10496 M = 5 23.3 -> 18.2,
-// N = 12288 M = 8 27.2 -> 20.1.
+// registers beyond that; from seven tiles on one unit is in flight, for the
+// same reason), and weights and activations under 2^31 bytes (its requests
+// with nothing to fetch sit past both).  It runs the 4-, 6- and 8-row
+// instances only: one or two rows reach activations of 96 KB at K of 24576
+// and more, where the pairs and per-phase kernels serve them.  Measured on
+// MI355X against the per-phase kernel at five to nine tiles: N = 9216
+// K = 17408 M = 8 25.8 -> 17.1 us, N = 10496 M = 5 23.3 -> 18.2, N = 12288
+// M = 8 27.2 -> 20.1, N = 12304 K = 12288 M = 8 23.1 -> 18.2, N = K = 17408
+// M = 8 38.4 -> 24.6.  (With resident activations over nine tiles, N = 17408
+// K = 5120, the two-subgroup pairs kernel stays faster: M = 8 10.5 against
+// 11.4 us.)
 template <int MMAX>
 inline bool segs_fit(const EvenGrid &g, uint32_t N, uint32_t K, uint32_t M) {
-  return g.tiles <= (MMAX <= 4 ? 4u : 6u) && (uint64_t)N * (K >> 7) * kBlockBytes < (1ull << 31) && (uint64_t)M * K * 2u < (1ull << 31);
+  return g.tiles <= (MMAX <= 4 ? 4u : 9u) && (uint64_t)N * (K >> 7) * kBlockBytes < (1ull << 31) && (uint64_t)M * K * 2u < (1ull << 31);
 }
 
 template <int MMAX>
@@ -1036,7 +1043,10 @@ hipError_t launch_segs(const EvenGrid &g, hipStream_t stream, const uint16_t *a,
   } else {
     if (g.tiles <= 4u) return launch_segs_t<MMAX, 4>(g.grid, stream, a, b, c, N, K, M);
     if (g.tiles <= 5u) return launch_segs_t<MMAX, 5>(g.grid, stream, a, b, c, N, K, M);
-    return launch_segs_t<MMAX, 6>(g.grid, stream, a, b, c, N, K, M);
+    if (g.tiles <= 6u) return launch_segs_t<MMAX, 6>(g.grid, stream, a, b, c, N, K, M);
+    if (g.tiles <= 7u) return launch_segs_t<MMAX, 7>(g.grid, stream, a, b, c, N, K, M);
+    if (g.tiles <= 8u) return launch_segs_t<MMAX, 8>(g.grid, stream, a, b, c, N, K, M);
+    return launch_segs_t<MMAX, 9>(g.grid, stream, a, b, c, N, K, M);
   }
 }
 
