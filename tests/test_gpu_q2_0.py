@@ -151,15 +151,14 @@ def test_ffn_shapes(oracle_mod, N, K):
                                    (9216, 17408, 8), (10496, 17408, 5), (12304, 12288, 8), (18440, 10240, 8),
                                    (8200, 20480, 4)])
 def test_large_k_batched_rows(oracle_mod, N, K, M):
-    """Activations too large for LDS: the segmented kernel where a
-    workgroup's share of the rows fits in nine 8-row tiles (N = 9216, 10496
-    and 12304 on 256 CUs give 36, 41 and 49 rows per workgroup: five, six and
-    seven tiles, the last with one unit in flight), else the per-phase kernel
-    with super-tiles of up to four tiles (N = 18440: 73 rows, ten tiles, three
-    super-tiles; N = 8200 M = 4: 33 rows, five tiles, beyond the 4-row
-    segmented instance): ragged N, every row bit-identical to its own M=1
-    launch (the resident-activation kernel) and within tolerance of the
-    oracle on a column sample."""
+    """Activations too large for LDS: the segmented kernel, over up to nine
+    8-row tiles per workgroup (N = 9216, 10496 and 12304 on 256 CUs give 36,
+    41 and 49 rows per workgroup: five, six and seven tiles, the last with
+    one unit in flight), and as launches over row ranges beyond that
+    (N = 18440: 73 rows, ten tiles, two ranges; N = 8200 M = 4: 33 rows, five
+    tiles, two ranges for the 4-row instance's limit of four): ragged N,
+    every row bit-identical to its own M=1 launch (the resident-activation
+    kernel) and within tolerance of the oracle on a column sample."""
     A, codes, d, packed = _case(31, N, K, M, salt=N + K)
     Bd = dev_u8(packed)
     got = q2_0_gpu(A, Bd, N, K)
@@ -242,6 +241,30 @@ def test_segmented_kernel_tiles_and_segments(oracle_mod, N, K, M):
     for m in range(M):
         assert np.array_equal(got[m:m + 1], q2_0_gpu(A[m:m + 1], Bd, N, K, single=True)), m
     cols = np.arange(N) if N <= 400 else np.union1d(gen.rng(953, N, K).choice(N, 256, replace=False), [N - 1])
+    check_parity(got[:, cols], oracle_mod.q2_0_gemv(A, codes[cols], d[cols]), f"q2_0 {N}x{K} M={M}")
+
+
+@pytest.mark.parametrize("N,K,M", [(37, 1280, 1), (37, 1280, 3), (300, 3328, 8), (1029, 3328, 5), (5120, 11008, 1),
+                                   (5120, 11008, 4), (5120, 11008, 8), (600, 13824, 2), (300, 81920, 1),
+                                   (200, 40960, 2)])
+def test_even_block_counts_and_one_or_two_large_rows(oracle_mod, N, K, M):
+    """K a multiple of 256 but not of 1024 (K / 128 = 10, 26, 86 and 108: odd
+    pair counts and waves owning different numbers of pairs) runs the
+    matrix-core kernels: the pairs kernel, and the segmented kernel where the
+    activations are large (K = 11008: 86 KB at M = 4, 176 KB at M = 8).  One
+    and two rows whose activations do not fit in LDS (K = 81920 and 40960:
+    160 KB) run the segmented kernel's 1- and 2-row instances.  Every row
+    bit-identical to its own M=1 launch, a canary row past M untouched, all
+    columns (or a sample holding the last one) within tolerance of the
+    oracle."""
+    A, codes, d, packed = _case(61, N, K, M, salt=N * 11 + K + M)
+    Bd = dev_u8(packed)
+    got = q2_0_gpu(A, Bd, N, K, extra_rows=1)
+    assert np.all(got[M] == CANARY)
+    got = got[:M]
+    for m in range(M):
+        assert np.array_equal(got[m:m + 1], q2_0_gpu(A[m:m + 1], Bd, N, K, single=True)), m
+    cols = np.arange(N) if N <= 400 else np.union1d(gen.rng(961, N, K).choice(N, 256, replace=False), [N - 1])
     check_parity(got[:, cols], oracle_mod.q2_0_gemv(A, codes[cols], d[cols]), f"q2_0 {N}x{K} M={M}")
 
 

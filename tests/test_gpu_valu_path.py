@@ -1,5 +1,5 @@
 """GPU parity of the vector-ALU Q2_0 kernel where the matrix-core kernel would
-normally run (K a multiple of 1024).
+normally run (K a multiple of 256 from 1024 up).
 
 The kernel choice is read once per process from WQD_Q2_0_VALU, so the check
 runs in a child process with that variable set.  The child compares against

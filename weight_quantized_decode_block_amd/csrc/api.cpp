@@ -65,18 +65,19 @@ constexpr uint32_t kTierWidths[WQD_Q2_0_TIER_COUNT] = WQD_Q2_0_TIER_WIDTHS;
 constexpr bool kTierExact[WQD_Q2_0_TIER_COUNT] = {false, true, true, true, false};
 constexpr uint32_t kTiersCompiled = (1u << WQD_Q2_0_TIER_COUNT) - 1u;
 
-// Kernel for Q2_0, chosen from K only (never M), so batched rows stay
-// bit-identical to M=1 rows: the matrix-core kernel when K is a multiple of
-// 1024, on the row tier q2_0_tier_width(m), else the vector-ALU kernel.  The
-// two kernels differ from each other only by fp32 rounding order; every tier
-// of the matrix-core kernel gives the same bits.  The presence of
-// WQD_Q2_0_VALU (any value; read once per process) forces the vector-ALU
-// kernel everywhere, for A/B runs.
+// Kernel for Q2_0, chosen from N and K only (never M), so batched rows stay
+// bit-identical to M=1 rows: the matrix-core kernels when K is a multiple of
+// 256 from 1024 up and the weights are under 2^31 bytes, on the row tier
+// q2_0_tier_width(m), else the vector-ALU kernel.  The two families differ
+// from each other only by fp32 rounding order; every matrix-core kernel and
+// tier gives the same bits.  The presence of WQD_Q2_0_VALU (any value; read
+// once per process) forces the vector-ALU kernel everywhere, for A/B runs.
 hipError_t launch_q2_0(const void *A, const void *B, void *C, uint32_t N, uint32_t K, uint32_t m,
                        hipStream_t stream) {
   static const bool valu = std::getenv("WQD_Q2_0_VALU") != nullptr;
   const uint32_t width = q2_0_tier_width(m);
-  if (!valu && width != 0 && wqd::q2_0_pairs_supports(K)) return wqd::launch_q2_0_pairs(A, B, C, N, K, m, width, stream);
+  if (!valu && width != 0 && wqd::q2_0_pairs_supports(N, K))
+    return wqd::launch_q2_0_pairs(A, B, C, N, K, m, width, stream);
   return wqd::launch_q2_0_valu(A, B, C, N, K, m, stream);
 }
 

@@ -9,7 +9,7 @@
 // the M=1 result).  The pages' kernels run the MACs on scalar FMAs; here they
 // run on v_mfma_f32_16x16x32_bf16 and the vector ALUs only decode.
 //
-// Work layout (requires K/128 to be a multiple of 8)
+// Work layout (requires K/128 to be even: whole block pairs)
 //   * A tile is 8 weight rows over the whole of K.  One MFMA covers two
 //     consecutive 128-k blocks (a block pair) of the tile: its 16 columns are
 //     (block half h, weight row r) = column 8h + r, and its 16 rows are (block
@@ -71,11 +71,6 @@ constexpr int kRows = 8;                                  // weight rows per til
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kSlots8 = 8;  // accumulation slots of a tile's block pairs
-constexpr int kPhaseBlocks = 16;                          // blocks per phase (8 waves x 2)
-constexpr int kPhaseRowBytes = kPhaseBlocks * kBlockBytes;  // 544 bytes of one weight row per phase
-constexpr int kWPitch = kPhaseRowBytes + 16;              // LDS row pitch (bank spread)
-constexpr int kAPhaseBytes = kPhaseBlocks * 256;          // 4096 bytes of one activation row per phase
-constexpr int kAPitch = kAPhaseBytes + 16;                // LDS pitch of a per-phase activation row
 constexpr uint32_t kLdsMax = 160u * 1024u;                // LDS per compute unit on gfx950
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
@@ -130,253 +125,14 @@ __device__ __forceinline__ f32x4_t neg_sum_chain(const bf16x8_t (&a)[4]) {
 }
 
 // ---------------------------------------------------------------------------
-// Per-phase kernel: for activations too large to keep in LDS.  Same unit
-// assignment, seeds, chains and reduction order as the pairs kernel below, so
-// both give the same bits.  One workgroup per CU owns an even share [r0, r1)
-// of the weight rows and walks it in super-tiles of TPP 8-row tiles (rows past
-// r1 re-read row r1 - 1 and are never stored), each in phases of 16 blocks:
-// a phase's TPP x 8 x 544 weight bytes and 16 blocks of every activation row
-// are fetched with 16-byte loads in which consecutive lanes read consecutive
-// addresses, kept DEPTH phases ahead in registers and written to one of two
-// LDS buffers (one barrier per phase).  Wave w computes block pair w of the
-// phase for every tile of the super-tile: the activations and their seed are
-// read and computed once and serve all TPP tiles, so the activation traffic
-// per weight row falls by TPP.
-// ---------------------------------------------------------------------------
-// LDS: [buffer 0][buffer 1][zero rows: 256][partial tiles: 2 x TPP x kWaves x
-// 2 x MMAX x 8 floats].  A buffer holds the phase's TPP x 8 weight rows, MMAX
-// activation-row segments and a 16-byte dummy slot at kDummy
-// (buffer-relative).
-template <int MMAX, int TPP>
-struct PhaseLayout {
-  static constexpr int kWRows = TPP * kRows;
-  static constexpr int kWSlots = (kWRows * (kPhaseRowBytes / 16) + kThreads - 1) / kThreads;
-  static constexpr int kSlots = kWSlots + (MMAX * (kAPhaseBytes / 16) + kThreads - 1) / kThreads;
-  static constexpr int kWBytesT = kWRows * kWPitch;
-  static constexpr int kDummy = kWBytesT + MMAX * kAPitch;
-  static constexpr int kBuf = kDummy + 16;
-  static constexpr int kZero = 2 * kBuf;
-  static constexpr int kPart = kZero + 256;
-  static constexpr int kFixed = kPart + 2 * TPP * kWaves * 2 * MMAX * kRows * 4;
-};
-
-// The 16-byte chunk slots of a thread.  Slots 0 .. WS-1 carry weight chunks:
-// chunk c = s * 512 + tid is row c / w of the super-tile, column c % w of the
-// row's phase segment (w = 34 chunks in a full phase, 17 in a half-length last
-// phase); its source row is resolved per super-tile.  Slots WS.. carry
-// per-phase activation chunks: k = (s - WS) * 512 + tid, row m = k / 256,
-// column k % 256.  Every slot keeps two precomputed variants: one for full
-// phases and one for the K tail's phase.  A chunk with nothing to fetch
-// re-reads an in-bounds chunk and goes to the dummy LDS slot.
-template <int S>
-struct Slots {
-  uint32_t src[2][S];  // weight slots: (row in super-tile) << 16 | byte column, or kNoRow; activation slots: offset
-  uint32_t dst[2][S];
-};
-constexpr uint32_t kNoRow = 0xFFFFFFFFu;
-
-template <int S, int WS, int WROWS>
-__device__ __forceinline__ void make_slots(Slots<S> &sl, uint32_t tid, uint32_t K, uint32_t M,
-                                           uint32_t tail_blocks, uint32_t dummy) {
-#pragma unroll
-  for (int v = 0; v < 2; ++v) {
-    const uint32_t pbn = v == 0 ? (uint32_t)kPhaseBlocks : tail_blocks;
-    const uint32_t wcols = pbn * kBlockBytes / 16u, acols = pbn * 16u;
-#pragma unroll
-    for (int s = 0; s < WS; ++s) {
-      const uint32_t c = (uint32_t)s * kThreads + tid;
-      const uint32_t r = c / wcols, col = c - r * wcols;
-      const bool in = r < (uint32_t)WROWS;
-      sl.src[v][s] = in ? (r << 16) | (16u * col) : kNoRow;
-      sl.dst[v][s] = in ? r * kWPitch + 16u * col : dummy;
-    }
-#pragma unroll
-    for (int s = WS; s < S; ++s) {
-      const uint32_t c = (uint32_t)(s - WS) * kThreads + tid;
-      const uint32_t m = c >> 8, col = c & 255u;
-      const bool in = m < M && col < acols;
-      sl.src[v][s] = in ? m * K * 2u + 16u * col : 0u;
-      sl.dst[v][s] = in ? (uint32_t)(WROWS * kWPitch) + m * kAPitch + 16u * col : dummy;
-    }
-  }
-}
-
-template <int MMAX, int DEPTH, int TPP>
-__global__ __launch_bounds__(kThreads) void q2_0_phase_kernel(const uint16_t *__restrict__ A,
-                                                              const uint8_t *__restrict__ B,
-                                                              uint16_t *__restrict__ C, uint32_t N, uint32_t K,
-                                                              uint32_t M) {
-  using L = PhaseLayout<MMAX, TPP>;
-  constexpr int S = L::kSlots;
-  constexpr int WS = L::kWSlots;
-  constexpr uint32_t kSpan = (uint32_t)L::kWRows;  // rows per super-tile
-  constexpr int NF = MMAX < 4 ? MMAX : 4;          // accumulator rows that can hold outputs
-  static_assert(DEPTH % 2 == 0, "buffer parity must be a compile-time function of the ring slot");
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const uint32_t tid = threadIdx.x;
-  const uint32_t lane = tid & 63u;
-  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const uint32_t i = lane & 15u, g = lane >> 4;
-  const uint32_t h = i >> 3, rw = i & 7u;  // MFMA column i = (block half h, weight row rw)
-  const uint32_t nb = K >> 7;
-  const uint32_t nphase = (nb + kPhaseBlocks - 1) / kPhaseBlocks;
-  const uint32_t tail_blocks = nb - (nphase - 1u) * kPhaseBlocks;  // 8 or 16
-  const size_t rb = (size_t)nb * kBlockBytes;
-  uint32_t r0, r1;
-  even_rows(N, blockIdx.x, gridDim.x, r0, r1);
-  // This workgroup's super-tiles start at r0, r0 + kSpan, ...; its phases
-  // form one sequence over them, and the load ring runs across super-tile
-  // boundaries so the next one's first phases are in flight when one ends.
-  const uint32_t my_tiles = (r1 - r0 + kSpan - 1u) / kSpan;
-  const uint32_t nq = my_tiles * nphase;
-
-  // zero region standing in for activation rows m >= M
-  if (tid < 16u) {
-    const u32x4_t z = {0u, 0u, 0u, 0u};
-    *reinterpret_cast<u32x4_t *>(lds + L::kZero + 16u * tid) = z;
-  }
-
-  Slots<S> sl;
-  make_slots<S, WS, (int)kSpan>(sl, tid, K, M, tail_blocks, L::kDummy);
-
-  // Sequence element q is phase q % nphase of this workgroup's super-tile
-  // q / nphase.  Past the end (q >= nq) it re-reads phase 0 of the first one,
-  // stored nowhere.
-  auto issue_q = [&](uint32_t q, u32x4_t(&r)[S]) __attribute__((always_inline)) {
-    const bool live = q < nq;
-    const uint32_t j = live ? q / nphase : 0u;
-    const uint32_t p = live ? q - j * nphase : 0u;
-    const bool tail = p + 1u == nphase;
-    const uint32_t base = r0 + j * kSpan;
-    const uint8_t *ab = reinterpret_cast<const uint8_t *>(A) + (size_t)p * kAPhaseBytes;
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const uint32_t v = tail ? sl.src[1][s] : sl.src[0][s];
-      if (s < WS) {
-        const uint32_t row = v == kNoRow ? r0 : min(base + (v >> 16), r1 - 1u);
-        const uint32_t col = v == kNoRow ? 0u : (v & 0xFFFFu);
-        r[s] = *reinterpret_cast<const u32x4_t *>(B + (size_t)row * rb + (size_t)p * kPhaseRowBytes + col);
-      } else {
-        r[s] = *reinterpret_cast<const u32x4_t *>(ab + v);
-      }
-    }
-  };
-
-  // This lane's MFMA operands within a phase: weight row rw of block 2*wave+h
-  // of tile t (its fp16 scale at wblk; its 8 code bytes inside the aligned
-  // 3-dword window at wwin, which `sel` extracts; + t * 8 rows), and
-  // activation row rw of the same block (or the zero region).
-  const uint32_t wblk = rw * kWPitch + 34u * h + 68u * wave;
-  const uint32_t wwin = rw * kWPitch + 32u * h + 8u * g + 68u * wave;  // code bytes at +2 (h = 0) or +4 (h = 1)
-  const uint32_t sel = h ? 0x07060504u : 0x05040302u;
-  const bool a_ok = rw < M;
-  const uint32_t a_lane = a_ok ? (uint32_t)L::kWBytesT + rw * kAPitch + (2u * wave + h) * 256u + 64u * g
-                               : (uint32_t)L::kZero + 64u * g;
-  const uint32_t a_buf = a_ok ? (uint32_t)L::kBuf : 0u;  // + per buffer
-  const bool lane_out = (g >> 1) == h;  // this lane's accumulator rows match its column's block half
-  float *part = reinterpret_cast<float *>(lds + L::kPart);  // [parity][tile][wave][half][m][r]
-
-  u32x4_t ring[DEPTH][S];
-#pragma unroll
-  for (int d = 0; d < DEPTH; ++d) issue_q((uint32_t)d, ring[d]);
-
-  f32x4_t acc[TPP];
-#pragma unroll
-  for (int t = 0; t < TPP; ++t) acc[t] = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
-  // The wave's block pair of the phase in buffer `parity`, for every tile.
-  auto unit = [&](uint32_t parity) __attribute__((always_inline)) {
-    const uint8_t *buf = lds + parity * L::kBuf;
-    const uint8_t *act = lds + a_lane + parity * a_buf;
-    bf16x8_t a[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) a[j] = *reinterpret_cast<const bf16x8_t *>(act + 16 * j);
-    const f32x4_t seed = neg_sum_chain(a);
-#pragma unroll
-    for (int t = 0; t < TPP; ++t) {
-      const uint8_t *tb = buf + t * (kRows * kWPitch);
-      const uint32_t *pw = reinterpret_cast<const uint32_t *>(tb + wwin);
-      const uint32_t c0 = pw[0], c1 = pw[1], c2 = pw[2];
-      const uint32_t w0 = __builtin_amdgcn_perm(c1, c0, sel);
-      const uint32_t w1 = __builtin_amdgcn_perm(c2, c1, sel);
-      const _Float16 d = *reinterpret_cast<const _Float16 *>(tb + wblk);
-      bf16x8_t b0, b1, b2, b3;
-      decode_word(w0, b0, b1);
-      decode_word(w1, b2, b3);
-      f32x4_t x = seed;
-      x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b0, x, 0, 0, 0);
-      x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], b1, x, 0, 0, 0);
-      x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2], b2, x, 0, 0, 0);
-      x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[3], b3, x, 0, 0, 0);
-#pragma unroll
-      for (int r = 0; r < NF; ++r) acc[t][r] = __builtin_fmaf((float)d, x[r], acc[t][r]);
-    }
-  };
-
-  // One sequence element: store its chunks into buffer `parity`, request the
-  // element DEPTH ahead into the same registers, compute, and finish the
-  // super-tile after its last phase.
-  auto step = [&](uint32_t q, uint32_t parity, u32x4_t(&r)[S]) __attribute__((always_inline)) {
-    uint8_t *buf = lds + parity * L::kBuf;
-    const uint32_t j = q / nphase, p = q - j * nphase;
-    const bool tail = p + 1u == nphase;
-    const uint32_t npairs = tail ? tail_blocks >> 1 : (uint32_t)kPhaseBlocks / 2u;
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const uint32_t dst = tail ? sl.dst[1][s] : sl.dst[0][s];
-      *reinterpret_cast<u32x4_t *>(buf + dst) = s < WS ? r[s] : permute_acts(r[s]);
-    }
-    issue_q(q + DEPTH, r);
-    __syncthreads();
-    if (wave < npairs) unit(parity);
-    if (tail) {  // super-tile done: add the 16 partial sums of each output in fixed order
-      const uint32_t par = j & 1u;
-      if (lane_out) {
-#pragma unroll
-        for (int t = 0; t < TPP; ++t) {
-#pragma unroll
-          for (int rr = 0; rr < NF; ++rr) {
-            const uint32_t m = 4u * (g & 1u) + rr;
-            if (m < M)
-              part[((((par * TPP + t) * kWaves + wave) * 2u + h) * MMAX + m) * kRows + rw] = acc[t][rr];
-          }
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < TPP; ++t) acc[t] = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
-      __syncthreads();
-      if (tid < M * kSpan) {
-        const uint32_t m = tid / kSpan, col = tid - m * kSpan;
-        const uint32_t t = col >> 3, r = col & 7u;
-        const uint32_t n = r0 + j * kSpan + col;
-        if (n < r1) {
-          const float *pp = part + ((par * TPP + t) * kWaves * 2u * MMAX + m) * kRows + r;
-          float v = pp[0];
-          for (uint32_t k = 1; k < 2u * kWaves; ++k) v = v + pp[k * MMAX * kRows];
-          store_out(C + (size_t)m * N + n, f32_to_bf16_rne(v));
-        }
-      }
-      // the next write of this parity's partials comes after another super-tile's barriers
-    }
-  };
-
-  uint32_t q = 0;
-  for (; q + DEPTH <= nq; q += DEPTH) {
-#pragma unroll
-    for (int d = 0; d < DEPTH; ++d) step(q + d, (uint32_t)(d & 1), ring[d]);
-  }
-#pragma unroll
-  for (int d = 0; d < DEPTH; ++d)
-    if (q + d < nq) step(q + d, (uint32_t)(d & 1), ring[d]);
-}
-
-// ---------------------------------------------------------------------------
 // Segmented kernel: for large activations (too large for LDS, or large
 // enough that staging them all before the first unit costs more than
-// staging them in pieces), with a workgroup's share of the rows in at most
-// TMAX tiles (up to nine).  The pairs kernel's units, seeds, chains and
+// staging them in pieces).  The pairs kernel's units, seeds, chains and
 // reduction order, so the same bits.
-//   * One workgroup per CU owns rows [r0, r1) (an even split of N) as T <= TMAX
-//     8-row tiles; rows past r1 re-read row r1 - 1 and are never stored.
+//   * One workgroup per CU owns rows [r0, r1) (an even split of N) as
+//     T <= TMAX 8-row tiles (TMAX up to nine; the launcher splits larger N
+//     into launches over row ranges); rows past r1 re-read row r1 - 1 and
+//     are never stored.
 //   * K is walked in segments of SP block pairs.  A segment of every
 //     activation row is staged in LDS once per workgroup (the pairs kernel's
 //     permuted order) into one of two buffers: the next segment's loads are
@@ -395,7 +151,9 @@ __global__ __launch_bounds__(kThreads) void q2_0_phase_kernel(const uint16_t *__
 //   * After the last segment the 16 partial sums of each output are added in
 //     LDS in the pairs kernel's order and rows m < M are stored.
 // Measured on MI355X (graph-replayed, cold weights) against the per-phase
-// kernel: N = 5120 K = 17408 M = 8 14.7 -> 11.9 us, M = 5 13.3 -> 10.8; and
+// kernel it replaced (super-tiles of up to four tiles walked in phases of 16
+// blocks, weights and activations both staged through LDS, one barrier per
+// phase): N = 5120 K = 17408 M = 8 14.7 -> 11.9 us, M = 5 13.3 -> 10.8; and
 // against the pairs kernel with the activations resident: K = 17408 M = 4
 // 12.7 -> 11.8, M = 3 12.5 -> 11.5, K = 8192 M = 8 9.1 -> 7.8, M = 6 9.1 ->
 // 7.5, K = 6144 M = 8 7.4 -> 6.7, K = 12288 M = 4 10.3 -> 9.9.  What did not
@@ -408,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void q2_0_phase_kernel(const uint16_t *__
 // reuse it at the end.
 template <int MMAX>
 struct SegShape {
-  static constexpr int kSP = MMAX <= 4 ? 32 : 16;                // block pairs per segment
+  static constexpr int kSP = MMAX == 4 ? 32 : 16;                // block pairs per segment
   static constexpr int kPitch = kSP * 512 + 16;                  // LDS pitch of an activation row segment
   static constexpr int kBuf = MMAX * kPitch;                     // one segment buffer
   static constexpr int kBuf0 = 256;                              // after the zero rows
@@ -427,7 +185,7 @@ template <int MMAX, int TMAX, int DEPTH>
 __global__ __launch_bounds__(kThreads) void q2_0_segs_kernel(const uint16_t *__restrict__ A,
                                                              const uint8_t *__restrict__ B,
                                                              uint16_t *__restrict__ C, uint32_t N, uint32_t K,
-                                                             uint32_t M) {
+                                                             uint32_t M, uint32_t ldc) {
   using G = SegShape<MMAX>;
   constexpr uint32_t kSP = G::kSP, kUps = kSP / kWaves;  // a wave's units per full segment
   constexpr int NF = MMAX < 4 ? MMAX : 4;                // accumulator rows that can hold outputs
@@ -601,7 +359,7 @@ __global__ __launch_bounds__(kThreads) void q2_0_segs_kernel(const uint16_t *__r
       const float *pp = part + ((t * kSlots8 * 2u) * MMAX + m) * kRows + col;
       float v = pp[0];
       for (uint32_t k = 1; k < 2u * kSlots8; ++k) v = v + pp[k * MMAX * kRows];
-      store_out(C + (size_t)m * N + n, f32_to_bf16_rne(v));
+      store_out(C + (size_t)m * ldc + n, f32_to_bf16_rne(v));
     }
   }
 }
@@ -645,7 +403,7 @@ struct PairRegs {
 
 // NW waves per workgroup (4 or 8).  Pair p of a tile belongs to accumulation
 // slot p % 8 whatever NW is: wave w owns pairs w, w + NW, ... and keeps one
-// accumulator per slot it owns, so the sums are those of the per-phase kernel.
+// accumulator per slot it owns, so the sums are those of the segmented kernel.
 // Weight bytes go straight from memory to the lanes that use them (buffer
 // loads bounded by the matrix size): lane (h, r, g) reads 12 bytes at
 // 68p + 32h + 8g of weight row r; the scale is taken from lane (h, r, 0)'s 12
@@ -967,32 +725,21 @@ hipError_t launch_pairs(uint32_t per_thread, int threads, size_t lds, int max_pe
                                                                          c, N, K, M);
 }
 
-template <int MMAX, int TPP>
-hipError_t launch_phase_tpp(uint32_t grid, hipStream_t stream, const uint16_t *a, const uint8_t *b, uint16_t *c,
-                            uint32_t N, uint32_t K, uint32_t M) {
-  constexpr auto kern = q2_0_phase_kernel<MMAX, 2, TPP>;
-  constexpr size_t lds = PhaseLayout<MMAX, TPP>::kFixed;
-  static_assert(lds <= kLdsMax, "per-phase kernel exceeds LDS");
-  static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax);
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, stream, a, b, c, N, K, M);
-  return hipGetLastError();
-}
-
 template <int MMAX, int TMAX>
 hipError_t launch_segs_t(uint32_t grid, hipStream_t stream, const uint16_t *a, const uint8_t *b, uint16_t *c,
-                         uint32_t N, uint32_t K, uint32_t M) {
+                         uint32_t N, uint32_t K, uint32_t M, uint32_t ldc) {
+  // one segment's units in flight, or one unit from seven tiles on (two would
+  // not fit in registers)
   constexpr auto kern = q2_0_segs_kernel<MMAX, TMAX, TMAX >= 7 ? 1 : SegShape<MMAX>::kSP / kWaves>;
   constexpr size_t lds = SegShape<MMAX>::kBytes;
   static const hipError_t attr =
       hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, stream, a, b, c, N, K, M);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, stream, a, b, c, N, K, M, ldc);
   return hipGetLastError();
 }
 
-// The one-workgroup-per-CU grid of the segmented and per-phase kernels: the
+// The one-workgroup-per-CU grid of the segmented kernel: the
 // rows split evenly over min(CUs, tiles) workgroups, and the tiles of one
 // workgroup's share.
 struct EvenGrid {
@@ -1014,64 +761,63 @@ inline hipError_t even_grid(uint32_t N, EvenGrid &g) {
   return hipSuccess;
 }
 
-// The segmented kernel's limits: a workgroup's rows in at most nine tiles
-// (four for the 4-row instance, whose deeper ring would not fit in
-// registers beyond that; from seven tiles on one unit is in flight, for the
-// same reason), and weights and activations under 2^31 bytes (its requests
-// with nothing to fetch sit past both).  It runs the 4-, 6- and 8-row
-// instances only: one or two rows reach activations of 96 KB at K of 24576
-// and more, where the pairs and per-phase kernels serve them.  Measured on
-// MI355X against the per-phase kernel at five to nine tiles: N = 9216
+// The segmented kernel takes at most nine tiles per workgroup (four for the
+// 4-row instance, whose deeper ring would not fit in registers beyond
+// that; from seven tiles on one unit is in flight, for the same reason).
+// Larger N runs as launches over consecutive row ranges, as few as that
+// allows, each a full walk over K (rows are independent, so the bits do not
+// change).  Measured on MI355X against the kernel it replaced, which walked
+// super-tiles of up to four tiles in phases of 16 blocks through LDS (one
+// barrier per phase, activations and weights both staged): N = 9216
 // K = 17408 M = 8 25.8 -> 17.1 us, N = 10496 M = 5 23.3 -> 18.2, N = 12288
 // M = 8 27.2 -> 20.1, N = 12304 K = 12288 M = 8 23.1 -> 18.2, N = K = 17408
-// M = 8 38.4 -> 24.6.  (With resident activations over nine tiles, N = 17408
-// K = 5120, the two-subgroup pairs kernel stays faster: M = 8 10.5 against
-// 11.4 us.)
+// M = 8 38.4 -> 24.6, N = 5120 M = 8 14.7 -> 11.9.  (With resident
+// activations over nine tiles, N = 17408 K = 5120, the two-subgroup pairs
+// kernel stays faster: M = 8 10.5 against 11.4 us.)
 template <int MMAX>
-inline bool segs_fit(const EvenGrid &g, uint32_t N, uint32_t K, uint32_t M) {
-  return g.tiles <= (MMAX <= 4 ? 4u : 9u) && (uint64_t)N * (K >> 7) * kBlockBytes < (1ull << 31) && (uint64_t)M * K * 2u < (1ull << 31);
+constexpr uint32_t kSegMaxTiles = MMAX == 4 ? 4u : 9u;
+
+template <int MMAX>
+hipError_t launch_segs_range(const EvenGrid &g, hipStream_t stream, const uint16_t *a, const uint8_t *b,
+                             uint16_t *c, uint32_t N, uint32_t K, uint32_t M, uint32_t ldc) {
+  if (g.tiles <= 1u) return launch_segs_t<MMAX, 1>(g.grid, stream, a, b, c, N, K, M, ldc);
+  if (g.tiles <= 2u) return launch_segs_t<MMAX, 2>(g.grid, stream, a, b, c, N, K, M, ldc);
+  if (g.tiles <= 3u) return launch_segs_t<MMAX, 3>(g.grid, stream, a, b, c, N, K, M, ldc);
+  if constexpr (MMAX == 4) {
+    return launch_segs_t<MMAX, 4>(g.grid, stream, a, b, c, N, K, M, ldc);
+  } else {
+    if (g.tiles <= 4u) return launch_segs_t<MMAX, 4>(g.grid, stream, a, b, c, N, K, M, ldc);
+    if (g.tiles <= 5u) return launch_segs_t<MMAX, 5>(g.grid, stream, a, b, c, N, K, M, ldc);
+    if (g.tiles <= 6u) return launch_segs_t<MMAX, 6>(g.grid, stream, a, b, c, N, K, M, ldc);
+    if (g.tiles <= 7u) return launch_segs_t<MMAX, 7>(g.grid, stream, a, b, c, N, K, M, ldc);
+    if (g.tiles <= 8u) return launch_segs_t<MMAX, 8>(g.grid, stream, a, b, c, N, K, M, ldc);
+    return launch_segs_t<MMAX, 9>(g.grid, stream, a, b, c, N, K, M, ldc);
+  }
 }
 
 template <int MMAX>
 hipError_t launch_segs(const EvenGrid &g, hipStream_t stream, const uint16_t *a, const uint8_t *b, uint16_t *c,
                        uint32_t N, uint32_t K, uint32_t M) {
-  if (g.tiles <= 1u) return launch_segs_t<MMAX, 1>(g.grid, stream, a, b, c, N, K, M);
-  if (g.tiles <= 2u) return launch_segs_t<MMAX, 2>(g.grid, stream, a, b, c, N, K, M);
-  if (g.tiles <= 3u) return launch_segs_t<MMAX, 3>(g.grid, stream, a, b, c, N, K, M);
-  if constexpr (MMAX <= 4) {
-    return launch_segs_t<MMAX, 4>(g.grid, stream, a, b, c, N, K, M);
-  } else {
-    if (g.tiles <= 4u) return launch_segs_t<MMAX, 4>(g.grid, stream, a, b, c, N, K, M);
-    if (g.tiles <= 5u) return launch_segs_t<MMAX, 5>(g.grid, stream, a, b, c, N, K, M);
-    if (g.tiles <= 6u) return launch_segs_t<MMAX, 6>(g.grid, stream, a, b, c, N, K, M);
-    if (g.tiles <= 7u) return launch_segs_t<MMAX, 7>(g.grid, stream, a, b, c, N, K, M);
-    if (g.tiles <= 8u) return launch_segs_t<MMAX, 8>(g.grid, stream, a, b, c, N, K, M);
-    return launch_segs_t<MMAX, 9>(g.grid, stream, a, b, c, N, K, M);
+  if (g.tiles <= kSegMaxTiles<MMAX>) return launch_segs_range<MMAX>(g, stream, a, b, c, N, K, M, N);
+  const size_t rb = (size_t)(K >> 7) * kBlockBytes;
+  uint32_t parts = (g.tiles + kSegMaxTiles<MMAX> - 1u) / kSegMaxTiles<MMAX>;
+  for (;; ++parts) {  // as few ranges as keep every range within the tile limit
+    const uint32_t len = (N + parts - 1u) / parts;
+    EvenGrid pg;
+    const hipError_t e = even_grid(len, pg);
+    if (e != hipSuccess) return e;
+    if (pg.tiles <= kSegMaxTiles<MMAX>) break;
   }
-}
-
-// Activations too large for LDS: the segmented kernel where a workgroup's
-// rows fit in its tiles, else per phase.  Per phase: one workgroup per CU
-// (one needs up to 135 KB of LDS at 8 rows), the rows split evenly;
-// super-tiles as wide as the share of rows needs, up to 4 tiles (32 rows),
-// so every CU streams the same bytes and fetches the activations once per
-// super-tile.
-template <int MMAX>
-hipError_t launch_phase(const uint16_t *a, const uint8_t *b, uint16_t *c, uint32_t N, uint32_t K, uint32_t M,
-                        hipStream_t stream) {
-  EvenGrid eg;
-  const hipError_t e = even_grid(N, eg);
-  if (e != hipSuccess) return e;
-  if constexpr (MMAX >= 4) {
-    if (segs_fit<MMAX>(eg, N, K, M)) return launch_segs<MMAX>(eg, stream, a, b, c, N, K, M);
+  const uint32_t len = (N + parts - 1u) / parts;
+  for (uint32_t r = 0; r < N; r += len) {
+    const uint32_t n = min(len, N - r);
+    EvenGrid pg;
+    hipError_t e = even_grid(n, pg);
+    if (e != hipSuccess) return e;
+    e = launch_segs_range<MMAX>(pg, stream, a, b + (size_t)r * rb, c + r, n, K, M, N);
+    if (e != hipSuccess) return e;
   }
-  const uint32_t grid = eg.grid, rows = eg.rows;
-  const uint32_t nsuper = (rows + 4u * kRows - 1u) / (4u * kRows);
-  const uint32_t tpp = (rows + kRows * nsuper - 1u) / (kRows * nsuper);
-  if (tpp <= 1u) return launch_phase_tpp<MMAX, 1>(grid, stream, a, b, c, N, K, M);
-  if (tpp <= 2u) return launch_phase_tpp<MMAX, 2>(grid, stream, a, b, c, N, K, M);
-  if (tpp <= 3u) return launch_phase_tpp<MMAX, 3>(grid, stream, a, b, c, N, K, M);
-  return launch_phase_tpp<MMAX, 4>(grid, stream, a, b, c, N, K, M);
+  return hipSuccess;
 }
 
 template <int MMAX>
@@ -1082,7 +828,6 @@ hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32
   const auto *b = static_cast<const uint8_t *>(B);
   auto *c = static_cast<uint16_t *>(C);
   constexpr int NW = 8;
-  const bool bounded = (uint64_t)N * (K >> 7) * kBlockBytes < (1ull << 32);  // buffer-load range
   const bool big = (uint64_t)N * (K >> 7) * kBlockBytes >= (16ull << 20);
   // Up to two workgroups per compute unit where the LDS allows it (measured
   // on MI355X, graph-replayed, cold weights: M = 1 5.28 -> 4.88 us at
@@ -1120,7 +865,7 @@ hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32
   // K = 5120, M = 6: 11.78 against 12.14 us for the 6-row instance).
   if constexpr (MMAX > 4) {
     const size_t lds2 = pair_lds_bytes<8, 2>(M, K);
-    if (big && lds2 <= kLdsMax && bounded) {
+    if (big && lds2 <= kLdsMax) {
       const uint32_t pt = (M * (K >> 3) + 1023u) / 1024u;
       const uint32_t half = (ntiles + 1u) / 2u;
       return launch_pairs<8, NW, 3, 2, 1>(pt, 1024, lds2, 1, half, stream, a, b, c, N, K, M);
@@ -1138,12 +883,11 @@ hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32
       EvenGrid eg;
       const hipError_t e = even_grid(N, eg);
       if (e != hipSuccess) return e;
-      if (eg.tiles >= 2u && eg.tiles <= 3u && segs_fit<MMAX>(eg, N, K, M))
-        return launch_segs<MMAX>(eg, stream, a, b, c, N, K, M);
+      if (eg.tiles >= 2u && eg.tiles <= 3u) return launch_segs<MMAX>(eg, stream, a, b, c, N, K, M);
     }
   }
   const size_t lds = pair_lds_bytes<MMAX>(M, K);
-  if (lds <= kLdsMax && bounded) {  // activations fit in LDS: the pairs kernel
+  if (lds <= kLdsMax) {  // activations fit in LDS: the pairs kernel
     const uint32_t per_thread = (M * (K >> 3) + 64 * NW - 1) / (64 * NW);  // staging chunks per thread
 #define WQD_PAIRS(D, L) \
   return launch_pairs<MMAX, NW, D, 1, L>(per_thread, 64 * NW, lds, kMaxPerCu, ntiles, stream, a, b, c, N, K, M)
@@ -1159,17 +903,24 @@ hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32
     }
 #undef WQD_PAIRS
   }
-  // else per phase (same bits)
-  return launch_phase<MMAX>(a, b, c, N, K, M, stream);
+  // else the segmented kernel (same bits)
+  EvenGrid eg;
+  const hipError_t e = even_grid(N, eg);
+  if (e != hipSuccess) return e;
+  return launch_segs<MMAX>(eg, stream, a, b, c, N, K, M);
 }
 
 }  // namespace
 
-bool q2_0_pairs_supports(uint32_t K) { return K >= 1024u && ((K >> 7) % 8u) == 0; }
+bool q2_0_pairs_supports(uint32_t N, uint32_t K) {
+  // whole block pairs, and weights within the buffer loads' 2^31-byte range
+  // (which also holds the segmented kernel's requests with nothing to fetch)
+  return K >= 1024u && ((K >> 7) % 2u) == 0 && (uint64_t)N * (K >> 7) * kBlockBytes < (1ull << 31);
+}
 
 hipError_t launch_q2_0_pairs(const void *A, const void *B, void *C, uint32_t N, uint32_t K, uint32_t m,
                              uint32_t width, hipStream_t stream) {
-  if (m == 0 || m > width) return hipErrorInvalidValue;
+  if (m == 0 || m > width || !q2_0_pairs_supports(N, K)) return hipErrorInvalidValue;
   switch (width) {
     case 1: return launch_mmax<1>(A, B, C, N, K, m, stream);
     case 2: return launch_mmax<2>(A, B, C, N, K, m, stream);

@@ -34,10 +34,11 @@ __device__ __forceinline__ void store_out(uint16_t *p, uint16_t v) {
 hipError_t launch_q2_0_valu(const void *A, const void *B, void *C, uint32_t N,
                             uint32_t K, uint32_t m, hipStream_t stream);
 
-// Same operation on the matrix-core kernel, 1..8 rows per launch, for K a
-// multiple of 1024 (q2_0_pairs_supports).  `width` (1, 2, 4, 6 or 8, at
-// least m) picks the compiled row tier; every tier gives a row the same bits.
-bool q2_0_pairs_supports(uint32_t K);
+// Same operation on the matrix-core kernels, 1..8 rows per launch, for K a
+// multiple of 256 from 1024 up and weights under 2^31 bytes
+// (q2_0_pairs_supports).  `width` (1, 2, 4, 6 or 8, at least m) picks the
+// compiled row tier; every tier gives a row the same bits.
+bool q2_0_pairs_supports(uint32_t N, uint32_t K);
 hipError_t launch_q2_0_pairs(const void *A, const void *B, void *C, uint32_t N,
                              uint32_t K, uint32_t m, uint32_t width, hipStream_t stream);
 
