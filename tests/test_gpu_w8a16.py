@@ -145,7 +145,7 @@ def test_ffn_shapes(oracle_mod, N, K):
 
 @pytest.mark.parametrize("N,K,M", [(5120, 17408, 5), (5120, 17408, 8), (5120, 17408, 12), (1000, 16512, 9),
                                    (17408, 9216, 10), (300, 17408, 7), (5120, 17408, 3), (8192, 8192, 8),
-                                   (5120, 6144, 8)])
+                                   (5120, 6144, 8), (20736, 10240, 8), (20744, 6144, 12)])
 def test_activations_larger_than_lds(oracle_mod, N, K, M):
     """Large activations are staged in segments of K: those larger than LDS
     (M x K x 2 bytes over 160 KB), and resident ones of 96 KB or more (more
@@ -154,7 +154,10 @@ def test_activations_larger_than_lds(oracle_mod, N, K, M):
     Every row equals its own M=1 call (which keeps all of A in LDS) bit for
     bit, the 64-row-band call gives the same bits, and sampled columns are
     within the parity bar.  Covers K not a multiple of 1024 (16512), a
-    workgroup with five 16-row tiles (N = 17408) and one tile (N = 300)."""
+    workgroup with five 16-row tiles (N = 17408) and one tile (N = 300), and
+    more than five tiles per workgroup, served as launches over ranges of
+    whole 128-row scale groups (N = 20736 and 20744: six tiles, two ranges,
+    the second of 20744 ending mid-group)."""
     from weight_quantized_decode_block_amd import wqd
     A, W, S = _case(31, N, K, M, salt=N + K)
     Wd, Sd = dev_u8(W), dev_f32(S)

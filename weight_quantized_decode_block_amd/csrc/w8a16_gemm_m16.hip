@@ -982,6 +982,36 @@ hipError_t launch_segs(const SegGrid &sg, hipStream_t stream, const void *A, con
   return launch_segs_t<MMAX, 5>(sg.grid, stream, A, W, S, C, M, N, K, lda, ldc, band);
 }
 
+// More than five 16-row tiles per workgroup: launches of the segmented kernel
+// over consecutive row ranges of whole 128-row scale groups, as few as keep
+// each within five tiles (rows are independent, so the bits do not change).
+// Measured on MI355X against the per-phase kernel it replaces there: N =
+// 20736 K = 10240 M = 8 58.1 -> 46.9 us, N = 20744 K = 6144 M = 12 50.4 ->
+// 31.8, N = 21000 K = 17408 M = 5 86.3 -> 72.1.
+template <int MMAX>
+hipError_t launch_segs_ranges(hipStream_t stream, const void *A, const void *W, const float *S, void *C, uint32_t M,
+                              uint32_t N, uint32_t K, uint32_t lda, uint32_t ldc) {
+  uint32_t len = 0;
+  for (uint32_t parts = 2;; ++parts) {
+    len = (((N + parts - 1u) / parts) + 127u) & ~127u;
+    SegGrid g;
+    const hipError_t e = seg_grid(len, 0u, g);
+    if (e != hipSuccess) return e;
+    if (g.tiles <= 5u) break;
+  }
+  const size_t nb = K >> 7;
+  for (uint32_t r = 0; r < N; r += len) {
+    const uint32_t n = min(len, N - r);
+    SegGrid g;
+    hipError_t e = seg_grid(n, 0u, g);
+    if (e != hipSuccess) return e;
+    e = launch_segs<MMAX>(g, stream, A, static_cast<const uint8_t *>(W) + (size_t)r * K, S + (size_t)(r >> 7) * nb,
+                          static_cast<uint16_t *>(C) + r, M, n, K, lda, ldc, 0u);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 }  // namespace
 
 hipError_t launch_w8a16_m16(const void *A, const void *W, const float *S, void *C, uint32_t M, uint32_t N,
@@ -1025,6 +1055,12 @@ hipError_t launch_w8a16_m16(const void *A, const void *W, const float *S, void *
     if (sg.tiles <= 5u) {
       if (M <= 8) return launch_segs<8>(sg, stream, A, W, S, C, M, N, K, lda, ldc, band);
       return launch_segs<16>(sg, stream, A, W, S, C, M, N, K, lda, ldc, band);
+    }
+    // more than five tiles per workgroup: row ranges (9..16 rows with up to
+    // 5 blocks per wave keep the registers kernel below)
+    if (band == 0u && !(M > 8 && nbw <= 5u)) {
+      if (M <= 8) return launch_segs_ranges<8>(stream, A, W, S, C, M, N, K, lda, ldc);
+      return launch_segs_ranges<16>(stream, A, W, S, C, M, N, K, lda, ldc);
     }
   }
   // 9..16 rows over more than five tiles per workgroup with up to 5 blocks per
