@@ -9,9 +9,17 @@
 // instruction's 16 rows) and the doc of w8a16_gemm_m16 (BF16 A [m,k],
 // BF16 C [m,n], rows >= m untouched).  The pages' Hopper design (mma.sync
 // m16n8k16, 32 columns and 128 threads per CTA, A staged with cp.async) is
-// not used; this kernel is laid out for gfx950 as follows.
+// not used.
 //
-// Work layout
+// Four kernels give the same bits (the same blocks per wave, chains and
+// reduction order) and are chosen by shape (launch_w8a16_m16 at the end):
+// the units kernel (up to 8 rows, activations resident in LDS), the
+// segmented kernel (large activations, and 9..16 rows), the registers kernel
+// (9..16 rows over more than five tiles per workgroup, K <= 5120), and the
+// per-phase kernel described next, for what the others cannot address
+// (weights of 2 GB and more, very wide activation row pitches).
+//
+// Per-phase work layout
 //   * A workgroup of 8 waves owns a tile of 16 weight rows and walks K in
 //     phases of up to 8 blocks (1024 k).  Each phase's bytes - 16 weight-row
 //     segments of 1 KB and the M activation-row segments of 2 KB - are fetched
