@@ -9,6 +9,11 @@
 // the M=1 result).  The pages' kernels run the MACs on scalar FMAs; here they
 // run on v_mfma_f32_16x16x32_bf16 and the vector ALUs only decode.
 //
+// Two kernels give the same bits (the same units, seeds, chains and
+// reduction order) and are chosen by shape (launch_mmax at the end): the
+// pairs kernel described next (activations resident in LDS), and the
+// segmented kernel for large activations (described at its definition).
+//
 // Work layout (requires K/128 to be even: whole block pairs)
 //   * A tile is 8 weight rows over the whole of K.  One MFMA covers two
 //     consecutive 128-k blocks (a block pair) of the tile: its 16 columns are
