@@ -79,9 +79,10 @@ __device__ __forceinline__ float dot2(uint32_t a, bf16x2_t t, float c) {
 // One 34-byte block as 9 dwords plus the selectors that undo its 0/2-byte
 // misalignment.
 struct Block {
-  uint32_t w[9];
-  uint32_t sel;   // v_perm selector yielding code word q from (w[q+1], w[q])
-  uint32_t dsh;   // shift of the fp16 scale inside w[0]
+  uint32_t w[8];
+  uint32_t lo, hi;  // the two halves of the ninth dword (w[8] = lo | hi << 16)
+  uint32_t sel;     // v_perm selector yielding code word q from (w[q+1], w[q])
+  uint32_t dsh;     // shift of the fp16 scale inside w[0]
 };
 
 __device__ __forceinline__ void load_block(const uint8_t *__restrict__ B, uint64_t off,
@@ -92,10 +93,14 @@ __device__ __forceinline__ void load_block(const uint8_t *__restrict__ B, uint64
   const u32x4a4 v1 = *reinterpret_cast<const u32x4a4 *>(p + 4);
   k.w[0] = v0.x; k.w[1] = v0.y; k.w[2] = v0.z; k.w[3] = v0.w;
   k.w[4] = v1.x; k.w[5] = v1.y; k.w[6] = v1.z; k.w[7] = v1.w;
-  if (o4 + 36 <= total)
-    k.w[8] = p[8];
-  else  // last block of the buffer, ending 2 bytes into this dword
-    k.w[8] = *reinterpret_cast<const uint16_t *>(p + 8);
+  // The ninth dword as two halves, with no branch and combined only where it
+  // is used (combining here would wait for these loads).  Only an odd block
+  // (starting 2 bytes into a dword) uses the upper half; the buffer's last
+  // block can end 2 bytes into this dword only when it is even, and then its
+  // upper half is read from an in-range address and never used.
+  const uint16_t *h = reinterpret_cast<const uint16_t *>(B);
+  k.lo = h[(o4 + 32) >> 1];
+  k.hi = h[(min(o4 + 34, total - 2)) >> 1];
   const bool odd = (off & 2) != 0;
   k.sel = odd ? 0x07060504u : 0x05040302u;
   k.dsh = odd ? 16u : 0u;
@@ -159,7 +164,7 @@ __device__ __forceinline__ void mac_block(const Block &k, const uint32_t *ap, co
   for (int m = 0; m < MC; ++m) s[m] = -asum[(size_t)m * tb + bl];
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
-    const uint32_t w = __builtin_amdgcn_perm(k.w[q + 1], k.w[q], k.sel);
+    const uint32_t w = __builtin_amdgcn_perm(q == 7 ? (k.lo | (k.hi << 16)) : k.w[q + 1], k.w[q], k.sel);
     const uint32_t x0 = w & 0x03030303u;
     const uint32_t x1 = (w >> 2) & 0x03030303u;
     const uint32_t x2 = (w >> 4) & 0x03030303u;
@@ -215,22 +220,35 @@ __global__ __launch_bounds__(kThreads) void q2_0_gemv_kernel(const uint16_t *__r
 #pragma unroll
   for (int m = 0; m < MC; ++m) acc[m] = 0.0f;
 
+  // Lane j's blocks of a tile are j, j + 8, ...: two of them in flight, each
+  // refilled in place after its MAC.  A lane whose block lies past the
+  // tile's last re-reads that last block (never used), so no request sits
+  // behind a per-lane branch; requests past the tile's last round of 8
+  // blocks are skipped (a condition the same for every lane).  Measured on
+  // MI355X against one block ahead with the requests behind per-lane branches
+  // (a register copy per block that waited for its request): N = 5120,
+  // K = 5248 M = 1 10.1 -> 9.4 us, M = 8 34.2 -> 33.2, and with the kernel
+  // forced, N = K = 5120 M = 1 9.1 -> 8.1, K = 17408 26.2 -> 23.1; small K
+  // unchanged (N = 32768 K = 512 4.44 against 4.49).
   for (uint32_t kb0 = 0; kb0 < nb; kb0 += tb) {
     const uint32_t tcount = min(tb, nb - kb0);
-    Block cur;
-    uint32_t bl = j;
-    if (row_ok && bl < tcount) load_block(B, row_off + (uint64_t)(kb0 + bl) * kBlockBytes, total, cur);
+    const uint32_t nk = (tcount + 7u) / 8u;  // rounds of 8 blocks (uniform)
+    auto fetch = [&](uint32_t bl, Block &k) __attribute__((always_inline)) {
+      load_block(B, row_off + (uint64_t)(kb0 + min(bl, tcount - 1u)) * kBlockBytes, total, k);
+    };
+    Block ring[2];
+    fetch(j, ring[0]);
+    if (nk > 1u) fetch(j + 8u, ring[1]);
     __syncthreads();  // all readers of the previous tile are done
     stage_tile<MC>(A, K, kb0, tcount, tb, ap, asum);
     __syncthreads();
-    if (row_ok) {
-      while (bl < tcount) {
-        const uint32_t nbl = bl + 8;
-        Block nxt;
-        if (nbl < tcount) load_block(B, row_off + (uint64_t)(kb0 + nbl) * kBlockBytes, total, nxt);
-        mac_block<MC>(cur, ap, asum, tb, bl, acc);
-        cur = nxt;
-        bl = nbl;
+    for (uint32_t k = 0; k < nk; k += 2u) {
+      const uint32_t bl0 = j + 8u * k, bl1 = bl0 + 8u;
+      if (row_ok && bl0 < tcount) mac_block<MC>(ring[0], ap, asum, tb, bl0, acc);
+      if (k + 2u < nk) fetch(bl0 + 16u, ring[0]);
+      if (k + 1u < nk) {
+        if (row_ok && bl1 < tcount) mac_block<MC>(ring[1], ap, asum, tb, bl1, acc);
+        if (k + 3u < nk) fetch(bl1 + 16u, ring[1]);
       }
     }
   }
