@@ -244,6 +244,28 @@ def test_segmented_kernel_tiles_and_segments(oracle_mod, N, K, M):
     check_parity(got[:, cols], oracle_mod.q2_0_gemv(A, codes[cols], d[cols]), f"q2_0 {N}x{K} M={M}")
 
 
+@pytest.mark.parametrize("N,K,M", [(9219, 17408, 8), (9000, 20480, 8), (12288, 17408, 7), (10496, 17408, 5),
+                                   (12304, 17408, 6), (12304, 17408, 8)])
+def test_segmented_two_group_form(oracle_mod, N, K, M):
+    """Five to seven tiles per workgroup at six or eight activation rows run the
+    segmented kernel's two-group form (16 waves, the tiles split between two
+    groups of 8 that own the same pairs): five tiles (N = 9219, a ragged last
+    tile; N = 9000 with K = 20480, full segments only), six (N = 12288, the
+    8-row instance at M = 7; N = 10496, the 6-row instance at M = 5) and seven
+    (N = 12304, both instances).  Every row bit-identical to its own M=1 launch
+    (the resident-activation kernel, 8 waves), a canary row past M untouched,
+    a sample of columns holding the last one within tolerance of the oracle."""
+    A, codes, d, packed = _case(67, N, K, M, salt=N * 13 + K + M)
+    Bd = dev_u8(packed)
+    got = q2_0_gpu(A, Bd, N, K, extra_rows=1)
+    assert np.all(got[M] == CANARY)
+    got = got[:M]
+    for m in range(M):
+        assert np.array_equal(got[m:m + 1], q2_0_gpu(A[m:m + 1], Bd, N, K, single=True)), m
+    cols = np.union1d(gen.rng(971, N, K).choice(N, 256, replace=False), [N - 1])
+    check_parity(got[:, cols], oracle_mod.q2_0_gemv(A, codes[cols], d[cols]), f"q2_0 {N}x{K} M={M}")
+
+
 @pytest.mark.parametrize("N,K,M", [(37, 1280, 1), (37, 1280, 3), (300, 3328, 8), (1029, 3328, 5), (5120, 11008, 1),
                                    (5120, 11008, 4), (5120, 11008, 8), (600, 13824, 2), (300, 81920, 1),
                                    (200, 40960, 2)])

@@ -12,7 +12,8 @@
 // Two kernels give the same bits (the same units, seeds, chains and
 // reduction order) and are chosen by shape (launch_mmax at the end): the
 // pairs kernel described next (activations resident in LDS), and the
-// segmented kernel for large activations (described at its definition).
+// segmented kernel for large activations (described at its definition, with
+// its 16-wave two-group form).
 //
 // Work layout (requires K/128 to be even: whole block pairs)
 //   * A tile is 8 weight rows over the whole of K.  One MFMA covers two
@@ -129,6 +130,30 @@ __device__ __forceinline__ f32x4_t neg_sum_chain(const bf16x8_t (&a)[4]) {
   return x;
 }
 
+// One tile's share of a unit of the segmented kernels: the lane's 12-byte
+// window w of the block pair, its 16 codes decoded and fed to four MFMA
+// seeded with -sum(a), then the product scaled by the block's fp16 scale
+// (taken from lane (h, r, 0) of the column) into the tile's accumulator.
+template <int NF>
+__device__ __forceinline__ void seg_tile(const u32x3_t &w, uint32_t sel, uint32_t i, uint32_t h, const f32x4_t &seed,
+                                         const bf16x8_t (&a)[4], f32x4_t &acc) {
+  const uint32_t w0 = __builtin_amdgcn_perm(w.y, w.x, sel);
+  const uint32_t w1 = __builtin_amdgcn_perm(w.z, w.y, sel);
+  const uint32_t own_d = h ? (w.x >> 16) : (w.x & 0xFFFFu);  // meaningful on lanes g = 0
+  const uint32_t dbits = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(i << 2), (int)own_d);
+  const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)dbits);
+  bf16x8_t b0, b1, b2, b3;
+  decode_word(w0, b0, b1);
+  decode_word(w1, b2, b3);
+  f32x4_t x = seed;
+  x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b0, x, 0, 0, 0);
+  x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], b1, x, 0, 0, 0);
+  x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2], b2, x, 0, 0, 0);
+  x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[3], b3, x, 0, 0, 0);
+#pragma unroll
+  for (int rr = 0; rr < NF; ++rr) acc[rr] = __builtin_fmaf((float)d, x[rr], acc[rr]);
+}
+
 // ---------------------------------------------------------------------------
 // Segmented kernel: for large activations (too large for LDS, or large
 // enough that staging them all before the first unit costs more than
@@ -169,16 +194,17 @@ __device__ __forceinline__ f32x4_t neg_sum_chain(const bf16x8_t (&a)[4]) {
 // of the barrier, so waves may run a segment apart (11.9 -> 12.4).
 // LDS: [zero rows: 256][segment buffer 0][segment buffer 1]; the partial sums
 // reuse it at the end.
-template <int MMAX>
+template <int MMAX, int NG = 1>
 struct SegShape {
   static constexpr int kSP = MMAX == 4 ? 32 : 16;                // block pairs per segment
   static constexpr int kPitch = kSP * 512 + 16;                  // LDS pitch of an activation row segment
   static constexpr int kBuf = MMAX * kPitch;                     // one segment buffer
   static constexpr int kBuf0 = 256;                              // after the zero rows
   static constexpr int kBytes = kBuf0 + 2 * kBuf;
-  static constexpr int kChunks = MMAX * kSP * 32 / kThreads;     // 16-byte chunks per thread per segment
+  static constexpr int kThr = kThreads * NG;                     // threads: NG groups of 8 waves
+  static constexpr int kChunks = MMAX * kSP * 32 / kThr;         // 16-byte chunks per thread per segment
   static_assert(kSP % kWaves == 0, "a wave must meet its pairs in ascending order");
-  static_assert(MMAX * kSP * 32 % kThreads == 0, "whole staging rounds");
+  static_assert(MMAX * kSP * 32 % kThr == 0, "whole staging rounds");
   static_assert(kBytes <= (int)kLdsMax, "two segment buffers must fit in LDS");
 };
 // Buffer offset of a request with nothing to fetch: beyond every weight and
@@ -292,24 +318,7 @@ __global__ __launch_bounds__(kThreads) void q2_0_segs_kernel(const uint16_t *__r
     for (int j = 0; j < 4; ++j) a[j] = *reinterpret_cast<const bf16x8_t *>(act + 16 * j);
     const f32x4_t seed = neg_sum_chain(a);
 #pragma unroll
-    for (int t = 0; t < TMAX; ++t) {
-      const u32x3_t w = r.w[t];
-      const uint32_t w0 = __builtin_amdgcn_perm(w.y, w.x, sel);
-      const uint32_t w1 = __builtin_amdgcn_perm(w.z, w.y, sel);
-      const uint32_t own_d = h ? (w.x >> 16) : (w.x & 0xFFFFu);  // meaningful on lanes g = 0
-      const uint32_t dbits = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(i << 2), (int)own_d);
-      const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)dbits);
-      bf16x8_t b0, b1, b2, b3;
-      decode_word(w0, b0, b1);
-      decode_word(w1, b2, b3);
-      f32x4_t x = seed;
-      x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b0, x, 0, 0, 0);
-      x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], b1, x, 0, 0, 0);
-      x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2], b2, x, 0, 0, 0);
-      x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[3], b3, x, 0, 0, 0);
-#pragma unroll
-      for (int rr = 0; rr < NF; ++rr) acc[t][rr] = __builtin_fmaf((float)d, x[rr], acc[t][rr]);
-    }
+    for (int t = 0; t < TMAX; ++t) seg_tile<NF>(r.w[t], sel, i, h, seed, a, acc[t]);
   };
 
   // Every segment but the last is full (each wave owns kUps of its pairs
@@ -357,6 +366,189 @@ __global__ __launch_bounds__(kThreads) void q2_0_segs_kernel(const uint16_t *__r
   __syncthreads();
   const uint32_t per = M * (uint32_t)kRows;
   for (uint32_t x = tid; x < T * per; x += kThreads) {  // (more outputs than threads from nine 8-row tiles on)
+    const uint32_t t = x / per, lt = x - t * per;
+    const uint32_t m = lt >> 3, col = lt & 7u;
+    const uint32_t n = r0 + (uint32_t)kRows * t + col;
+    if (n < r1) {
+      const float *pp = part + ((t * kSlots8 * 2u) * MMAX + m) * kRows + col;
+      float v = pp[0];
+      for (uint32_t k = 1; k < 2u * kSlots8; ++k) v = v + pp[k * MMAX * kRows];
+      store_out(C + (size_t)m * ldc + n, f32_to_bf16_rne(v));
+    }
+  }
+}
+
+// Two-group form of the segmented kernel for five to seven tiles per
+// workgroup at six or eight rows: 16 waves, where waves w and w + 8 own the
+// same pairs (w, w + 8, ...) and split the tiles, group 0 taking tiles 0, 2,
+// 4, ... and group 1 tiles 1, 3, 5, ...; each group runs its own seed chains.
+// Every chain, slot and reduction step is that of the 8-wave form, so the
+// bits are the same; what changes is four waves per SIMD instead of two
+// (each with half the registers, one unit in flight) to hide the latency of
+// the decode-MFMA chains.  Measured on MI355X (graph-replayed, cold weights)
+// against the 8-wave form: N = 12304 K = 12288 M = 8 (seven tiles) 18.2 ->
+// 15.6-15.8 us, N = 12288 K = 17408 M = 8 (six) 20.3 -> 18.5, N = 9216
+// K = 17408 M = 8 (five) 17.0 -> 16.3, N = 10496 K = 17408 M = 5 (six, the
+// 6-row instance) 18.4 -> 17.5.  At three and four tiles (the 1:2 or 2:2
+// split) and at eight or nine (registers) it was slower or even.
+template <int MMAX, int TMAX>
+__global__ __launch_bounds__(2 * kThreads) void q2_0_segs_groups_kernel(const uint16_t *__restrict__ A,
+                                                                       const uint8_t *__restrict__ B,
+                                                                       uint16_t *__restrict__ C, uint32_t N,
+                                                                       uint32_t K, uint32_t M, uint32_t ldc) {
+  constexpr int NG = 2;
+  using G = SegShape<MMAX, NG>;
+  constexpr uint32_t kSP = G::kSP, kUps = kSP / kWaves;  // a wave's units per full segment
+  constexpr uint32_t kThr = G::kThr;
+  constexpr int NF = MMAX < 4 ? MMAX : 4;
+  static_assert(TMAX * kSlots8 * 2 * MMAX * kRows * 4 <= G::kBytes, "the partial sums reuse the buffers");
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const uint32_t tid = threadIdx.x;
+  const uint32_t lane = tid & 63u;
+  const uint32_t wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t wave = wave_all & (uint32_t)(kWaves - 1);  // owns pairs wave, wave + 8, ...
+  const uint32_t grp = wave_all / (uint32_t)kWaves;         // owns tiles grp, grp + 2, ...
+  const uint32_t i = lane & 15u, g = lane >> 4;
+  const uint32_t h = i >> 3, rw = i & 7u;
+  const uint32_t nb = K >> 7, npairs = nb >> 1;
+  const uint32_t nseg = (npairs + kSP - 1u) / kSP;
+
+  // staging as in the 8-wave form over twice the threads; each chunk's
+  // offsets are recomputed when used (registers are the scarce resource here)
+  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(A), (short)0, (int)(M * K * 2u), 0x00020000);
+  u32x4_t av[G::kChunks];
+  auto a_src = [&](int u) {
+    const uint32_t c = (uint32_t)u * kThr + tid;
+    const uint32_t m = c / (32u * kSP), col = c % (32u * kSP);
+    return m < M ? m * 2u * K + 16u * col : kPastEnd;
+  };
+  auto a_dst = [&](int u) {
+    const uint32_t c = (uint32_t)u * kThr + tid;
+    const uint32_t m = c / (32u * kSP), col = c % (32u * kSP);
+    return (uint32_t)G::kBuf0 + m * (uint32_t)G::kPitch + 16u * col;
+  };
+  auto stage_load = [&](uint32_t s) {
+#pragma unroll
+    for (int u = 0; u < G::kChunks; ++u)
+      av[u] = __builtin_amdgcn_raw_buffer_load_b128(arsrc, a_src(u), s * kSP * 512u, 0);
+  };
+  auto stage_store = [&](uint32_t s) {
+    const uint32_t boff = (s & 1u) * (uint32_t)G::kBuf;
+#pragma unroll
+    for (int u = 0; u < G::kChunks; ++u) *reinterpret_cast<u32x4_t *>(lds + a_dst(u) + boff) = permute_acts(av[u]);
+  };
+  stage_load(0u);
+
+  uint32_t r0, r1;
+  even_rows(N, blockIdx.x, gridDim.x, r0, r1);
+  const uint32_t T = (r1 - r0 + (uint32_t)kRows - 1u) / (uint32_t)kRows;  // <= TMAX (checked by the launcher)
+  const uint32_t rb = nb * kBlockBytes;
+  const uint32_t nq = npairs > wave ? (npairs - wave + kWaves - 1u) / kWaves : 0u;  // the wave's pairs
+  const __amdgpu_buffer_rsrc_t wrsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(B), (short)0, (int)(N * rb), 0x00020000);
+  const bool a_ok = rw < M;
+  const uint32_t a_lane = a_ok ? (uint32_t)G::kBuf0 + rw * G::kPitch + h * 256u + 64u * g : 64u * g;
+  const uint32_t a_buf = a_ok ? (uint32_t)G::kBuf : 0u;
+  const uint32_t a_stride = a_ok ? 512u : 0u;
+  const uint32_t sel = h ? 0x07060504u : 0x05040302u;
+  const bool lane_out = (g >> 1) == h;
+  float *part = reinterpret_cast<float *>(lds);  // [tile][slot][half][m][r], after the last segment
+
+  // The group's TG tiles: its own requests, registers and chains; both
+  // groups meet the same barriers.
+  auto run = [&](auto TGc) {
+    constexpr int TG = decltype(TGc)::value;
+    uint32_t voff[TG];
+#pragma unroll
+    for (int k = 0; k < TG; ++k) {
+      const uint32_t t = grp + (uint32_t)NG * (uint32_t)k;
+      const uint32_t row = min(r0 + (uint32_t)kRows * t + rw, r1 - 1u);
+      voff[k] = t < T ? row * rb + 32u * h + 8u * g : kPastEnd;
+    }
+    struct SegRegs {
+      u32x3_t w[TG];
+    };
+    auto issue = [&](uint32_t q) {  // unit q of this wave: pair wave + 8 q, for the group's tiles
+      const bool live = q < nq;
+      const uint32_t soff = 68u * (wave + kWaves * q);
+      SegRegs r;
+#pragma unroll
+      for (int k = 0; k < TG; ++k)
+        r.w[k] = __builtin_amdgcn_raw_buffer_load_b96(wrsrc, live ? voff[k] : kPastEnd, soff, 0);
+      return r;
+    };
+
+    SegRegs ring = issue(0u);
+    if (tid < 16u) {  // zero region standing in for activation rows m >= M
+      const u32x4_t z = {0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4_t *>(lds + 16u * tid) = z;
+    }
+    stage_store(0u);
+    __syncthreads();
+    stage_load(min(1u, nseg - 1u));
+
+    f32x4_t acc[TG];
+#pragma unroll
+    for (int k = 0; k < TG; ++k) acc[k] = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
+    auto unit = [&](const SegRegs &r, uint32_t q, uint32_t s) {
+      const uint32_t pl = wave + kWaves * q - s * kSP;
+      const uint8_t *act = lds + a_lane + (s & 1u) * a_buf + a_stride * pl;
+      bf16x8_t a[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[j] = *reinterpret_cast<const bf16x8_t *>(act + 16 * j);
+      const f32x4_t seed = neg_sum_chain(a);
+#pragma unroll
+      for (int k = 0; k < TG; ++k) seg_tile<NF>(r.w[k], sel, i, h, seed, a, acc[k]);
+    };
+
+    // full segments straight-line, the last one peeled (as in the 8-wave form)
+    const uint32_t nlast = nseg - 1u;
+    uint32_t q = 0;
+    for (uint32_t s = 0; s < nlast; ++s) {
+#pragma unroll
+      for (int u = 0; u < (int)kUps; ++u) {
+        unit(ring, q, s);
+        ring = issue(q + 1u);
+        ++q;
+      }
+      stage_store(s + 1u);
+      __syncthreads();
+      stage_load(min(s + 2u, nlast));
+    }
+#pragma unroll
+    for (int u = 0; u < (int)kUps; ++u) {
+      if (q < nq) {
+        unit(ring, q, nlast);
+        if (q + 1u < nq) ring = issue(q + 1u);
+      }
+      ++q;
+    }
+
+    __syncthreads();  // every wave is done with the segment buffers
+    if (lane_out) {
+#pragma unroll
+      for (int k = 0; k < TG; ++k) {
+        const uint32_t t = grp + (uint32_t)NG * (uint32_t)k;
+        if (t < T) {
+#pragma unroll
+          for (int rr = 0; rr < NF; ++rr) {
+            const uint32_t m = 4u * (g & 1u) + rr;
+            if (m < M) part[(((t * kSlots8 + wave) * 2u + h) * MMAX + m) * kRows + rw] = acc[k][rr];
+          }
+        }
+      }
+    }
+  };
+  if (grp == 0u)
+    run(std::integral_constant<int, (TMAX + 1) / 2>{});
+  else
+    run(std::integral_constant<int, TMAX / 2>{});
+
+  // the 16 partial sums of each output, added in slot and half order
+  __syncthreads();
+  const uint32_t per = M * (uint32_t)kRows;
+  for (uint32_t x = tid; x < T * per; x += kThr) {
     const uint32_t t = x / per, lt = x - t * per;
     const uint32_t m = lt >> 3, col = lt & 7u;
     const uint32_t n = r0 + (uint32_t)kRows * t + col;
@@ -730,18 +922,28 @@ hipError_t launch_pairs(uint32_t per_thread, int threads, size_t lds, int max_pe
                                                                          c, N, K, M);
 }
 
+template <auto KERN, uint32_t THREADS, size_t LDS>
+hipError_t launch_segs_k(uint32_t grid, hipStream_t stream, const uint16_t *a, const uint8_t *b, uint16_t *c,
+                         uint32_t N, uint32_t K, uint32_t M, uint32_t ldc) {
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void *>(KERN), hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(KERN, dim3(grid), dim3(THREADS), LDS, stream, a, b, c, N, K, M, ldc);
+  return hipGetLastError();
+}
+
 template <int MMAX, int TMAX>
 hipError_t launch_segs_t(uint32_t grid, hipStream_t stream, const uint16_t *a, const uint8_t *b, uint16_t *c,
                          uint32_t N, uint32_t K, uint32_t M, uint32_t ldc) {
-  // one segment's units in flight, or one unit from seven tiles on (two would
-  // not fit in registers)
-  constexpr auto kern = q2_0_segs_kernel<MMAX, TMAX, TMAX >= 7 ? 1 : SegShape<MMAX>::kSP / kWaves>;
   constexpr size_t lds = SegShape<MMAX>::kBytes;
-  static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, stream, a, b, c, N, K, M, ldc);
-  return hipGetLastError();
+  if constexpr ((MMAX == 6 || MMAX == 8) && TMAX >= 5 && TMAX <= 7) {  // the two-group form
+    return launch_segs_k<q2_0_segs_groups_kernel<MMAX, TMAX>, 2u * kThreads, lds>(grid, stream, a, b, c, N, K, M, ldc);
+  } else {
+    // one segment's units in flight, or one unit from seven tiles on (two would
+    // not fit in registers)
+    return launch_segs_k<q2_0_segs_kernel<MMAX, TMAX, TMAX >= 7 ? 1 : SegShape<MMAX>::kSP / kWaves>, kThreads, lds>(
+        grid, stream, a, b, c, N, K, M, ldc);
+  }
 }
 
 // The one-workgroup-per-CU grid of the segmented kernel: the
