@@ -84,10 +84,12 @@ def test_every_staging_tier_rows_bit_identical(oracle_mod, N, K, M):
 
 
 @pytest.mark.parametrize("N,K,M", [(300, 640, 13), (4100, 5120, 16), (20480, 2048, 9), (20736, 1024, 12),
-                                   (20744, 5120, 16)])
+                                   (20744, 5120, 16), (12000, 5120, 16), (10240, 17408, 12), (16400, 6144, 11)])
 def test_nine_to_sixteen_rows_kernels(oracle_mod, N, K, M):
     """Nine to sixteen rows: the segmented kernel over one, two and five
-    16-row tiles per workgroup (on 256 CUs: N = 300, 4100, 20480), and the
+    16-row tiles per workgroup (on 256 CUs: N = 300, 4100, 20480), its
+    two-group form from three tiles on (N = 12000 and 10240: three, 47 and 40
+    rows; N = 16400: five, the last one ragged), and the
     registers kernel where a workgroup's rows need more than five tiles
     (N = 20736, K = 1024: 81 rows, six tiles; N = 20744, K = 5120: five
     blocks per wave).  Every row bit-identical to its own M=1 call (the units

@@ -14,7 +14,8 @@
 // Four kernels give the same bits (the same blocks per wave, chains and
 // reduction order) and are chosen by shape (launch_w8a16_m16 at the end):
 // the units kernel (up to 8 rows, activations resident in LDS), the
-// segmented kernel (large activations, and 9..16 rows), the registers kernel
+// segmented kernel (large activations, and 9..16 rows; a 16-wave form of it
+// for 9..16 rows over three to five tiles), the registers kernel
 // (9..16 rows over more than five tiles per workgroup, K <= 5120), and the
 // per-phase kernel described next, for what the others cannot address
 // (weights of 2 GB and more, very wide activation row pitches).
@@ -760,14 +761,15 @@ struct SegRegs {
   float s[TMAX];               // the block's scale for this lane's row, per tile
 };
 
-template <int MMAX>
+template <int MMAX, int NG = 1>
 struct SegShape {
   static constexpr int kSB = MMAX <= 8 ? 32 : 16;             // blocks per segment
   static constexpr int kPitch = kSB * 256 + 16;               // LDS pitch of an activation row segment
   static constexpr int kBuf = MMAX * kPitch;                  // one segment buffer
-  static constexpr int kChunks = MMAX * kSB * 16 / kThreads;  // 16-byte chunks per thread per segment
+  static constexpr int kThr = kThreads * NG;                  // threads: NG groups of 8 waves
+  static constexpr int kChunks = MMAX * kSB * 16 / kThr;      // 16-byte chunks per thread per segment
   static_assert(kSB % kWaves == 0, "a wave must meet its blocks in ascending order");
-  static_assert(MMAX * kSB * 16 % kThreads == 0, "whole staging rounds");
+  static_assert(MMAX * kSB * 16 % kThr == 0, "whole staging rounds");
 };
 
 template <int MMAX, int TMAX, int DEPTH>
@@ -941,20 +943,217 @@ __global__ __launch_bounds__(kThreads) void w8a16_segs_kernel(const uint16_t *__
   }
 }
 
+// Two-group form of the segmented kernel: 16 waves, where waves w and w + 8
+// own the same blocks (w, w + 8, ...) and split the workgroup's tiles, group
+// 0 taking tiles 0, 2, 4, ... and group 1 tiles 1, 3, ...  Every chain, fold
+// and reduction step is that of the 8-wave form, so the bits are the same;
+// what changes is four waves per SIMD instead of two (each with half the
+// registers) to hide the latency of the convert-MFMA-fold chains.  Measured
+// on MI355X (graph-replayed, cold weights) against the 8-wave form, it pays
+// only for 9 to 16 rows over three or more tiles: N = 17408 K = 5120 M = 16
+// (five tiles) 21.9 -> 21.3 us, N = 10240 K = 17408 M = 12 (three) 37.6 ->
+// 37.0.  Over two tiles (a 1 : 1 split) and for up to 8 rows it was slower:
+// N = K = 5120 M = 16 10.1 -> 10.5, N = 5120 K = 17408 M = 16 25.6 -> 26.7,
+// M = 8 23.1 -> 23.3, N = 10240 K = 17408 M = 8 36.2 -> 36.4 (the weights'
+// 16-row loads keep the address unit busier here than in the Q2_0 kernel).
+template <int MMAX, int TMAX, int DEPTH>
+__global__ __launch_bounds__(2 * kThreads) void w8a16_segs_groups_kernel(
+    const uint16_t *__restrict__ A, const uint8_t *__restrict__ W, const float *__restrict__ S,
+    uint16_t *__restrict__ C, uint32_t M, uint32_t N, uint32_t K, uint32_t lda, uint32_t ldc, uint32_t band) {
+  constexpr int NG = 2;
+  using G = SegShape<MMAX, NG>;
+  constexpr int NF = MMAX < 4 ? MMAX : 4;
+  constexpr uint32_t kSB = G::kSB, kUps = kSB / kWaves;
+  constexpr uint32_t kThr = G::kThr;
+  static_assert(kUps % DEPTH == 0, "a segment's units fill whole rounds of the ring");
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const uint32_t tid = threadIdx.x;
+  const uint32_t lane = tid & 63u;
+  const uint32_t wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t wave = wave_all & (uint32_t)(kWaves - 1);  // owns blocks wave, wave + 8, ...
+  const uint32_t grp = wave_all / (uint32_t)kWaves;         // owns tiles grp, grp + 2, ...
+  const uint32_t i = lane & 15u, g = lane >> 4;
+  const uint32_t nb = K >> 7;
+
+  // staging as in the 8-wave form over twice the threads; each chunk's
+  // offsets are recomputed when used (registers are the scarce resource here)
+  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(A), (short)0, (int)(((M - 1u) * lda + K) * 2u), 0x00020000);
+  u32x4_t av[G::kChunks];
+  auto a_src = [&](int u) {
+    const uint32_t c = (uint32_t)u * kThr + tid;
+    const uint32_t m = c / (kSB * 16u), col = c % (kSB * 16u);
+    return m < M ? m * lda * 2u + 16u * col : kPastEnd;
+  };
+  auto a_dst = [&](int u) {
+    const uint32_t c = (uint32_t)u * kThr + tid;
+    const uint32_t m = c / (kSB * 16u), col = c % (kSB * 16u);
+    return m * (uint32_t)G::kPitch + 16u * col;
+  };
+  auto stage_load = [&](uint32_t sg) {
+#pragma unroll
+    for (int u = 0; u < G::kChunks; ++u)
+      av[u] = __builtin_amdgcn_raw_buffer_load_b128(arsrc, a_src(u), sg * kSB * 256u, 0);
+  };
+  auto stage_store = [&](uint32_t sg) {
+    uint8_t *buf = lds + (sg & 1u) * G::kBuf;
+#pragma unroll
+    for (int u = 0; u < G::kChunks; ++u) *reinterpret_cast<u32x4_t *>(buf + a_dst(u)) = av[u];
+  };
+  stage_load(0u);
+
+  uint32_t r0, r1;
+  if (band == 0u) {
+    even_rows(N, blockIdx.x, gridDim.x, r0, r1);
+  } else {
+    r0 = blockIdx.x * 16u * band;
+    r1 = min(r0 + 16u * band, N);
+  }
+  const uint32_t T = (r1 - r0 + 15u) >> 4;  // <= TMAX (checked by the launcher)
+  const uint32_t nseg = (nb + kSB - 1u) / kSB;
+  const uint32_t nq = nb > wave ? (nb - wave + kWaves - 1) / kWaves : 0u;  // the wave's blocks
+  const __amdgpu_buffer_rsrc_t wrsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(W), (short)0, (int)(N * K), 0x00020000);
+  const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float *>(S), (short)0, (int)(((N + 127u) >> 7) * nb * 4u), 0x00020000);
+  const uint32_t w_lane = 32u * g;
+  const uint32_t a_lane = (i < M ? i : 0u) * G::kPitch + 64u * g;  // rows >= M read row 0, never stored
+  float *part = reinterpret_cast<float *>(lds);                      // [tile][wave][m][16], at the end
+
+  // The group's TG tiles: its own requests, registers and chains; both
+  // groups meet the same barriers.
+  auto run = [&](auto TGc) {
+    constexpr int TG = decltype(TGc)::value;
+    uint32_t lq = 0;  // next unit to request: block wave + 8 lq of the group's tiles
+    auto issue_next = [&]() {
+      const bool live = lq < nq;
+      const uint32_t b = live ? wave + kWaves * lq : 0u;
+      SegRegs<MMAX, TG> r;
+#pragma unroll
+      for (int k = 0; k < TG; ++k) {
+        const uint32_t t = grp + (uint32_t)NG * (uint32_t)k;
+        const uint32_t row = r0 + 16u * t + i;
+        const bool in = live && t < T && row < r1;
+        const uint32_t voff = in ? row * K + w_lane : kPastEnd;
+        r.w0[k] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, voff, 128u * b, 0);
+        r.w1[k] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, voff + 16u, 128u * b, 0);
+        const uint32_t srow = (row < r1 ? row : r1 - 1u) >> 7;
+        r.s[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                               srsrc, in ? srow * nb * 4u : kPastEnd, 4u * b, 0));
+      }
+      ++lq;
+      return r;
+    };
+
+    SegRegs<MMAX, TG> ring[DEPTH];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) ring[d] = issue_next();
+    stage_store(0u);
+    __syncthreads();
+    const uint32_t nlast = nseg - 1u;
+    stage_load(min(1u, nlast));
+
+    f32x4_t outer[TG];
+#pragma unroll
+    for (int k = 0; k < TG; ++k) outer[k] = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
+    auto unit = [&](const SegRegs<MMAX, TG> &r, uint32_t b, uint32_t sg) {
+      const uint8_t *act = lds + (sg & 1u) * G::kBuf + a_lane + 256u * (b - sg * kSB);
+      bf16x8_t a[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[j] = *reinterpret_cast<const bf16x8_t *>(act + 16 * j);
+#pragma unroll
+      for (int k = 0; k < TG; ++k) {
+        f32x4_t x = {0.0f, 0.0f, 0.0f, 0.0f};
+        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], weights8(r.w0[k].x, r.w0[k].y), x, 0, 0, 0);
+        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], weights8(r.w0[k].z, r.w0[k].w), x, 0, 0, 0);
+        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2], weights8(r.w1[k].x, r.w1[k].y), x, 0, 0, 0);
+        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[3], weights8(r.w1[k].z, r.w1[k].w), x, 0, 0, 0);
+#pragma unroll
+        for (int rr = 0; rr < NF; ++rr) outer[k][rr] = __fadd_rn(outer[k][rr], __fmul_rn(r.s[k], x[rr]));
+      }
+    };
+
+    // full segments straight-line, the last one peeled (as in the 8-wave form)
+    uint32_t q = 0;
+    for (uint32_t sg = 0; sg < nlast; ++sg) {
+#pragma unroll
+      for (int u = 0; u < (int)kUps; ++u) {
+        unit(ring[u % DEPTH], wave + kWaves * q, sg);
+        ring[u % DEPTH] = issue_next();
+        ++q;
+      }
+      stage_store(sg + 1u);
+      __syncthreads();
+      stage_load(min(sg + 2u, nlast));
+    }
+#pragma unroll
+    for (int u = 0; u < (int)kUps; ++u) {
+      if (q < nq) {
+        unit(ring[u % DEPTH], wave + kWaves * q, nlast);
+        if (q + DEPTH < nq) ring[u % DEPTH] = issue_next();
+      }
+      ++q;
+    }
+
+    __syncthreads();  // every wave is done with the segment buffers
+#pragma unroll
+    for (int k = 0; k < TG; ++k) {
+      const uint32_t t = grp + (uint32_t)NG * (uint32_t)k;
+      if (t < T) {
+#pragma unroll
+        for (int rr = 0; rr < NF; ++rr) {
+          const uint32_t m = 4u * g + rr;
+          if (m < M) part[((t * kWaves + wave) * MMAX + m) * 16u + i] = outer[k][rr];
+        }
+      }
+    }
+  };
+  if (grp == 0u)
+    run(std::integral_constant<int, (TMAX + 1) / 2>{});
+  else
+    run(std::integral_constant<int, TMAX / 2>{});
+
+  // the 8 waves' partial tiles, added in wave order
+  __syncthreads();
+  if (tid < M * 16u) {
+    const uint32_t m = tid >> 4, col = tid & 15u;
+    for (uint32_t t = 0; t < T; ++t) {
+      const uint32_t n = r0 + 16u * t + col;
+      if (n < r1) {
+        const float *pp = part + (t * kWaves * MMAX + m) * 16u + col;
+        float v = pp[0];
+        for (uint32_t w = 1; w < kWaves; ++w) v = v + pp[w * MMAX * 16u];
+        C[(size_t)m * ldc + n] = f32_to_bf16_rne(v);
+      }
+    }
+  }
+}
+
+template <auto KERN, uint32_t THREADS, size_t LDS>
+hipError_t launch_segs_k(uint32_t grid, hipStream_t stream, const void *A, const void *W, const float *S, void *C,
+                         uint32_t M, uint32_t N, uint32_t K, uint32_t lda, uint32_t ldc, uint32_t band) {
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void *>(KERN), hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(KERN, dim3(grid), dim3(THREADS), LDS, stream, static_cast<const uint16_t *>(A),
+                     static_cast<const uint8_t *>(W), S, static_cast<uint16_t *>(C), M, N, K, lda, ldc, band);
+  return hipGetLastError();
+}
+
 template <int MMAX, int TMAX>
 hipError_t launch_segs_t(uint32_t grid, hipStream_t stream, const void *A, const void *W, const float *S, void *C,
                          uint32_t M, uint32_t N, uint32_t K, uint32_t lda, uint32_t ldc, uint32_t band) {
-  // two units in flight, one at five tiles (where two would not fit in registers)
-  constexpr auto kern = w8a16_segs_kernel<MMAX, TMAX, TMAX >= 5 ? 1 : 2>;
   constexpr size_t lds = 2u * SegShape<MMAX>::kBuf;
   static_assert(lds <= 160u * 1024u, "two segment buffers must fit in LDS");
   static_assert((size_t)TMAX * kWaves * MMAX * 16u * 4u <= lds, "the partial tiles reuse the segment buffers");
-  static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, stream, static_cast<const uint16_t *>(A),
-                     static_cast<const uint8_t *>(W), S, static_cast<uint16_t *>(C), M, N, K, lda, ldc, band);
-  return hipGetLastError();
+  if constexpr (MMAX == 16 && TMAX >= 3) {  // the two-group form, two units in flight up to two tiles a group
+    return launch_segs_k<w8a16_segs_groups_kernel<MMAX, TMAX, (TMAX + 1) / 2 <= 2 ? 2 : 1>, 2u * kThreads, lds>(
+        grid, stream, A, W, S, C, M, N, K, lda, ldc, band);
+  } else {
+    // two units in flight, one at five tiles (where two would not fit in registers)
+    return launch_segs_k<w8a16_segs_kernel<MMAX, TMAX, TMAX >= 5 ? 1 : 2>, kThreads, lds>(grid, stream, A, W, S, C, M,
+                                                                                          N, K, lda, ldc, band);
+  }
 }
 
 // Tiles per workgroup of the segmented kernel's grid: one workgroup per CU
