@@ -379,7 +379,7 @@ def profile_facts(kernel_src: str, name: str) -> dict:
 def main():
     args = parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(the kernels would shard by output rows; see the design notes). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)

@@ -43,7 +43,7 @@ extern "C" {
 #define WQD_EINVAL        1  /* a size or count outside the documented range */
 #define WQD_ENULL         2  /* a required pointer is NULL */
 #define WQD_EALIGN        3  /* a pointer lacks the documented alignment */
-#define WQD_EUNSUPPORTED  4  /* valid input this build does not implement */
+#define WQD_EUNSUPPORTED  4  /* valid input this library does not implement */
 #define WQD_ENODEV        5  /* no usable HIP device */
 #define WQD_EHIP          6  /* a HIP runtime error; its text is in wqd_last_error() */
 
