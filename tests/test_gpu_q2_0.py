@@ -245,14 +245,16 @@ def test_segmented_kernel_tiles_and_segments(oracle_mod, N, K, M):
 
 
 @pytest.mark.parametrize("N,K,M", [(9219, 17408, 8), (9000, 20480, 8), (12288, 17408, 7), (10496, 17408, 5),
-                                   (12304, 17408, 6), (12304, 17408, 8)])
+                                   (12304, 17408, 6), (12304, 17408, 8), (8200, 17408, 8)])
 def test_segmented_two_group_form(oracle_mod, N, K, M):
     """Five to seven tiles per workgroup at six or eight activation rows run the
     segmented kernel's two-group form (16 waves, the tiles split between two
     groups of 8 that own the same pairs): five tiles (N = 9219, a ragged last
-    tile; N = 9000 with K = 20480, full segments only), six (N = 12288, the
-    8-row instance at M = 7; N = 10496, the 6-row instance at M = 5) and seven
-    (N = 12304, both instances).  Every row bit-identical to its own M=1 launch
+    tile; N = 9000 with K = 20480, full segments only; N = 8200, 33 rows on
+    some workgroups and 32 on others, so that group 0's third tile is real on
+    some and empty on others), six (N = 12288, the 8-row instance at M = 7;
+    N = 10496, the 6-row instance at M = 5) and seven (N = 12304, both
+    instances).  Every row bit-identical to its own M=1 launch
     (the resident-activation kernel, 8 waves), a canary row past M untouched,
     a sample of columns holding the last one within tolerance of the oracle."""
     A, codes, d, packed = _case(67, N, K, M, salt=N * 13 + K + M)
