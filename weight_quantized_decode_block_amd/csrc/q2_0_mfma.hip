@@ -389,8 +389,12 @@ __global__ __launch_bounds__(kThreads) void q2_0_segs_kernel(const uint16_t *__r
 // against the 8-wave form: N = 12304 K = 12288 M = 8 (seven tiles) 18.2 ->
 // 15.6-15.8 us, N = 12288 K = 17408 M = 8 (six) 20.3 -> 18.5, N = 9216
 // K = 17408 M = 8 (five) 17.0 -> 16.3, N = 10496 K = 17408 M = 5 (six, the
-// 6-row instance) 18.4 -> 17.5.  At three and four tiles (the 1:2 or 2:2
-// split) and at eight or nine (registers) it was slower or even.
+// 6-row instance) 18.4 -> 17.5.  At two to four tiles it was mixed within
+// 3 %, and at eight or nine (registers) slower or even.  It is a kernel of
+// its own rather than a template switch of the 8-wave one because the same
+// restructuring applied there changed that kernel's register allocation and
+// cost it 3 % (N = 5120 K = 17408 M = 8); the shared per-tile chain
+// (seg_tile) leaves its machine code as it was.
 template <int MMAX, int TMAX>
 __global__ __launch_bounds__(2 * kThreads) void q2_0_segs_groups_kernel(const uint16_t *__restrict__ A,
                                                                        const uint8_t *__restrict__ B,

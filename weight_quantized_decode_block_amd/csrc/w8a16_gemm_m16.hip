@@ -956,6 +956,8 @@ __global__ __launch_bounds__(kThreads) void w8a16_segs_kernel(const uint16_t *__
 // N = K = 5120 M = 16 10.1 -> 10.5, N = 5120 K = 17408 M = 16 25.6 -> 26.7,
 // M = 8 23.1 -> 23.3, N = 10240 K = 17408 M = 8 36.2 -> 36.4 (the weights'
 // 16-row loads keep the address unit busier here than in the Q2_0 kernel).
+// A kernel of its own, like the Q2_0 one, so that the 8-wave form's machine
+// code stays as measured.
 template <int MMAX, int TMAX, int DEPTH>
 __global__ __launch_bounds__(2 * kThreads) void w8a16_segs_groups_kernel(
     const uint16_t *__restrict__ A, const uint8_t *__restrict__ W, const float *__restrict__ S,
