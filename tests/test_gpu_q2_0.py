@@ -244,6 +244,29 @@ def test_segmented_kernel_tiles_and_segments(oracle_mod, N, K, M):
     check_parity(got[:, cols], oracle_mod.q2_0_gemv(A, codes[cols], d[cols]), f"q2_0 {N}x{K} M={M}")
 
 
+@pytest.mark.parametrize("N,K,M", [(5120, 17408, 2), (4100, 16384, 2), (12288, 20480, 2), (20480, 16384, 2),
+                                   (8192, 17408, 4), (8192, 17408, 3)])
+def test_segmented_kernel_two_rows_and_four_row_tiles(oracle_mod, N, K, M):
+    """Two rows whose activations are 64 KB or more (K >= 16384) run the
+    segmented kernel's 2-row instance over two to nine tiles per workgroup
+    (on 256 CUs: N = 5120 and 4100, three, 20 and 17 rows; N = 12288, six),
+    but not over ten (N = 20480 stays with the resident-activation kernel);
+    three or four rows of 96 KB or more over four tiles run its 4-row
+    instance (N = 8192, K = 17408).  Every
+    row bit-identical to its own M=1 launch (the resident-activation kernel),
+    a canary row past M untouched, a sample of columns holding the last one
+    within tolerance of the oracle."""
+    A, codes, d, packed = _case(71, N, K, M, salt=N * 17 + K + M)
+    Bd = dev_u8(packed)
+    got = q2_0_gpu(A, Bd, N, K, extra_rows=1)
+    assert np.all(got[M] == CANARY)
+    got = got[:M]
+    for m in range(M):
+        assert np.array_equal(got[m:m + 1], q2_0_gpu(A[m:m + 1], Bd, N, K, single=True)), m
+    cols = np.union1d(gen.rng(977, N, K).choice(N, 256, replace=False), [N - 1])
+    check_parity(got[:, cols], oracle_mod.q2_0_gemv(A, codes[cols], d[cols]), f"q2_0 {N}x{K} M={M}")
+
+
 @pytest.mark.parametrize("N,K,M", [(9219, 17408, 8), (9000, 20480, 8), (12288, 17408, 7), (10496, 17408, 5),
                                    (12304, 17408, 6), (12304, 17408, 8), (8200, 17408, 8)])
 def test_segmented_two_group_form(oracle_mod, N, K, M):

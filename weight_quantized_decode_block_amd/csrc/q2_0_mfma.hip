@@ -1082,19 +1082,42 @@ hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32
       return launch_pairs<8, NW, 3, 2, 1>(pt, 1024, lds2, 1, half, stream, a, b, c, N, K, M);
     }
   }
-  // Activations of 96 KB or more over two or three tiles per workgroup: the
-  // segmented kernel stages them in pieces behind the first units instead of
-  // all before them (measured in its description; at one tile per workgroup,
-  // N = 2048 K = 17408 M = 4, the pairs kernel stays faster, 7.0 against 7.5
-  // us, at four tiles, N = K = 8192 M = 8, the two tie, and with smaller
-  // activations the pairs kernel is faster: N = 5120 K = 12288 M = 2 8.0
-  // against 8.5, N = K = 8192 M = 4 8.9 against 10.0).
+  // Activations of 96 KB or more over two or three tiles per workgroup (four
+  // for the 4-row instance): the segmented kernel stages them in pieces
+  // behind the first units instead of all before them (measured in its
+  // description; at one tile per workgroup, N = 2048 K = 17408 M = 4, the
+  // pairs kernel stays faster, 7.0 against 7.5 us, at four tiles, N = K =
+  // 8192 M = 8, the two tie, and with smaller activations the pairs kernel is
+  // faster: N = 5120 K = 12288 M = 2 8.0 against 8.5, N = K = 8192 M = 4 8.9
+  // against 10.0).  Four tiles at three or four rows: N = 8192 K = 17408
+  // M = 4 15.75 -> 14.67 us, M = 3 15.52 -> 14.47 (N = 7168 K = 20480 M = 4
+  // even).
   if constexpr (MMAX >= 4) {
     if ((uint64_t)M * K * 2u >= 96u * 1024u) {
       EvenGrid eg;
       const hipError_t e = even_grid(N, eg);
       if (e != hipSuccess) return e;
-      if (eg.tiles >= 2u && eg.tiles <= 3u) return launch_segs<MMAX>(eg, stream, a, b, c, N, K, M);
+      if (eg.tiles >= 2u && eg.tiles <= (MMAX == 4 ? 4u : 3u)) return launch_segs<MMAX>(eg, stream, a, b, c, N, K, M);
+    }
+  }
+  // Two rows of 64 KB or more (K >= 16384) over two to nine tiles per
+  // workgroup (one launch): the segmented kernel too.  At K >= 16384 two rows leave LDS for
+  // one pairs workgroup per CU, whose 8 waves then walk 8 or more pairs per
+  // tile; the segmented kernel's units serve all of a workgroup's tiles.
+  // Measured (graph-replayed, cold weights): N = 5120 K = 17408 9.93 -> 8.73
+  // us, N = 8192 13.28 -> 11.46, N = 10240 14.62 -> 13.82, N = 14336 18.42
+  // -> 17.79, N = 5120 K = 20480 13.12 -> 10.29, N = 12288 K = 20480 23.15
+  // -> 19.91, N = K = 17408 21.94 -> 21.88, N = 8192 K = 16384 even; below
+  // K = 16384 the pairs kernel stays faster (N = 5120 K = 12288 7.72 against
+  // 7.97, K = 8192 6.05 against 6.45), and so it does beyond nine tiles, where
+  // the segmented kernel would take two launches (N = 20480 K = 16384 25.8
+  // against 30.5).
+  if constexpr (MMAX == 2) {
+    if ((uint64_t)M * K * 2u >= 64u * 1024u) {
+      EvenGrid eg;
+      const hipError_t e = even_grid(N, eg);
+      if (e != hipSuccess) return e;
+      if (eg.tiles >= 2u && eg.tiles <= kSegMaxTiles<MMAX>) return launch_segs<MMAX>(eg, stream, a, b, c, N, K, M);
     }
   }
   const size_t lds = pair_lds_bytes<MMAX>(M, K);
