@@ -1101,9 +1101,11 @@ hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32
     }
   }
   // Two rows of 64 KB or more (K >= 16384) over two to nine tiles per
-  // workgroup (one launch): the segmented kernel too.  At K >= 16384 two rows leave LDS for
-  // one pairs workgroup per CU, whose 8 waves then walk 8 or more pairs per
-  // tile; the segmented kernel's units serve all of a workgroup's tiles.
+  // workgroup (one launch): the segmented kernel too.  There a pairs
+  // workgroup stages 64 KB or more before its first unit and each of its
+  // waves walks eight or more pairs per tile, while the segmented kernel
+  // stages in pieces behind its first units and serves all of a workgroup's
+  // tiles from each unit's activations and seed.
   // Measured (graph-replayed, cold weights): N = 5120 K = 17408 9.93 -> 8.73
   // us, N = 8192 13.28 -> 11.46, N = 10240 14.62 -> 13.82, N = 14336 18.42
   // -> 17.79, N = 5120 K = 20480 13.12 -> 10.29, N = 12288 K = 20480 23.15
