@@ -1091,9 +1091,13 @@ hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32
   // faster: N = 5120 K = 12288 M = 2 8.0 against 8.5, N = K = 8192 M = 4 8.9
   // against 10.0).  Four tiles at three or four rows: N = 8192 K = 17408
   // M = 4 15.75 -> 14.67 us, M = 3 15.52 -> 14.47 (N = 7168 K = 20480 M = 4
-  // even).
+  // even).  Five to eight rows from K = 6144 on take it from 60 KB (one pairs
+  // workgroup per CU there): N = 5120 K = 7168 M = 6 8.14 -> 6.39 us, K = 6144
+  // M = 7 7.64 -> 6.68, K = 8192 M = 5 8.05 -> 7.40, N = 4096 K = 7168 M = 5
+  // 6.19 -> 5.45 (K = 6144 M = 5 and N = 6144 M = 6 even); at K = 5120 the
+  // pairs kernel stays (N = 5120 M = 6 5.68 against 5.93).
   if constexpr (MMAX >= 4) {
-    if ((uint64_t)M * K * 2u >= 96u * 1024u) {
+    if ((uint64_t)M * K * 2u >= 96u * 1024u || (M >= 5u && K >= 6144u && (uint64_t)M * K * 2u >= 60u * 1024u)) {
       EvenGrid eg;
       const hipError_t e = even_grid(N, eg);
       if (e != hipSuccess) return e;
