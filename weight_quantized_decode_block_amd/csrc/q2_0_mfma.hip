@@ -1095,9 +1095,13 @@ hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32
   // workgroup per CU there): N = 5120 K = 7168 M = 6 8.14 -> 6.39 us, K = 6144
   // M = 7 7.64 -> 6.68, K = 8192 M = 5 8.05 -> 7.40, N = 4096 K = 7168 M = 5
   // 6.19 -> 5.45 (K = 6144 M = 5 and N = 6144 M = 6 even); at K = 5120 the
-  // pairs kernel stays (N = 5120 M = 6 5.68 against 5.93).
+  // pairs kernel stays (N = 5120 M = 6 5.68 against 5.93).  Three or four
+  // rows from 84 KB on: N = 5120 K = 14336 M = 3 11.21 -> 9.61, K = 11264
+  // M = 4 9.51 -> 8.99 (at 80 KB, K = 10240 M = 4, the pairs kernel stays:
+  // 8.40 against 8.78).
   if constexpr (MMAX >= 4) {
-    if ((uint64_t)M * K * 2u >= 96u * 1024u || (M >= 5u && K >= 6144u && (uint64_t)M * K * 2u >= 60u * 1024u)) {
+    const uint64_t a_bytes = (uint64_t)M * K * 2u;
+    if (a_bytes >= (MMAX == 4 ? 84u : 96u) * 1024u || (M >= 5u && K >= 6144u && a_bytes >= 60u * 1024u)) {
       EvenGrid eg;
       const hipError_t e = even_grid(N, eg);
       if (e != hipSuccess) return e;
