@@ -147,12 +147,14 @@ def test_ffn_shapes(oracle_mod, N, K):
 
 @pytest.mark.parametrize("N,K,M", [(5120, 17408, 5), (5120, 17408, 8), (5120, 17408, 12), (1000, 16512, 9),
                                    (17408, 9216, 10), (300, 17408, 7), (5120, 17408, 3), (8192, 8192, 8),
-                                   (5120, 6144, 8), (20736, 10240, 8), (20744, 6144, 12)])
+                                   (5120, 6144, 8), (20736, 10240, 8), (20744, 6144, 12), (5120, 7168, 6),
+                                   (5120, 6144, 7)])
 def test_activations_larger_than_lds(oracle_mod, N, K, M):
     """Large activations are staged in segments of K: those larger than LDS
-    (M x K x 2 bytes over 160 KB), and resident ones of 96 KB or more (more
-    than 100 KB below five rows) over two or three 16-row tiles per workgroup
-    (N = 5120 K = 17408 M = 3, N = K = 8192 M = 8, N = 5120 K = 6144 M = 8).
+    (M x K x 2 bytes over 160 KB), and resident ones of 96 KB or more (84 KB
+    at six to eight rows, more than 100 KB below five rows) over two or three
+    16-row tiles per workgroup (N = 5120 K = 17408 M = 3, N = K = 8192 M = 8,
+    N = 5120 K = 6144 M = 8 and 7, N = 5120 K = 7168 M = 6).
     Every row equals its own M=1 call (which keeps all of A in LDS) bit for
     bit, the 64-row-band call gives the same bits, and sampled columns are
     within the parity bar.  Covers K not a multiple of 1024 (16512), a

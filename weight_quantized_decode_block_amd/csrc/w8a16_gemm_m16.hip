@@ -1237,10 +1237,14 @@ hipError_t launch_w8a16_m16(const void *A, const void *W, const float *S, void *
   // us, K = 8192 M = 6 13.4 -> 12.5, N = K = 8192 M = 8 18.2 -> 17.4), more
   // than 100 KB at fewer (N = 5120 K = 17408 M = 4 22.5 -> 21.6, M = 3 22.3 ->
   // 21.5; at 96 KB, K = 12288 M = 4, 17.0 against 17.2, and at one tile per
-  // workgroup, N = 4096, 12.9 against 14.9, the units kernel stays faster).
+  // workgroup, N = 4096, 12.9 against 14.9, the units kernel stays faster),
+  // and from 84 KB at six to eight rows (N = 5120 K = 7168 M = 6 12.14 ->
+  // 10.99, K = 6144 M = 7 11.16 -> 10.00; at five rows below 96 KB the units
+  // kernel stays: K = 8192 11.57 against 12.40, K = 6144 9.19 against 9.99).
   const bool seg_ok = bounded && (uint64_t)(M - 1u) * lda + K < (1ull << 30);  // (its activation range fits an int)
   const uint64_t a_bytes = (uint64_t)M * K * 2u;
-  if (seg_ok && M <= 8 && ((M >= 5 && a_bytes >= 96u * 1024u) || a_bytes > 100u * 1024u)) {
+  if (seg_ok && M <= 8 &&
+      ((M >= 6 && a_bytes >= 84u * 1024u) || (M >= 5 && a_bytes >= 96u * 1024u) || a_bytes > 100u * 1024u)) {
     SegGrid sg;
     const hipError_t e = seg_grid(N, band, sg);
     if (e != hipSuccess) return e;
