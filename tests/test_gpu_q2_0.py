@@ -273,7 +273,8 @@ def test_segmented_kernel_extra_routes(oracle_mod, N, K, M):
 
 
 @pytest.mark.parametrize("N,K,M", [(9219, 17408, 8), (9000, 20480, 8), (12288, 17408, 7), (10496, 17408, 5),
-                                   (12304, 17408, 6), (12304, 17408, 8), (8200, 17408, 8)])
+                                   (12304, 17408, 6), (12304, 17408, 8), (8200, 17408, 8), (12288, 5120, 8),
+                                   (9216, 5120, 8), (12288, 4096, 5), (14336, 5120, 6)])
 def test_segmented_two_group_form(oracle_mod, N, K, M):
     """Five to seven tiles per workgroup at six or eight activation rows run the
     segmented kernel's two-group form (16 waves, the tiles split between two
@@ -282,7 +283,9 @@ def test_segmented_two_group_form(oracle_mod, N, K, M):
     some workgroups and 32 on others, so that group 0's third tile is real on
     some and empty on others), six (N = 12288, the 8-row instance at M = 7;
     N = 10496, the 6-row instance at M = 5) and seven (N = 12304, both
-    instances).  Every row bit-identical to its own M=1 launch
+    instances); also with resident activations (K = 4096 and 5120, N = 9216
+    to 14336, where it runs ahead of both forms of the resident-activation
+    kernel).  Every row bit-identical to its own M=1 launch
     (the resident-activation kernel, 8 waves), a canary row past M untouched,
     a sample of columns holding the last one within tolerance of the oracle."""
     A, codes, d, packed = _case(67, N, K, M, salt=N * 13 + K + M)

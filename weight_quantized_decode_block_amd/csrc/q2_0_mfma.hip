@@ -1074,6 +1074,22 @@ hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32
   // N = K = 5120 one group stays faster, 6.74 against 7.31).  The 8-row
   // instance serves the 6-row tier here too (the same bits; N = 17408,
   // K = 5120, M = 6: 11.78 against 12.14 us for the 6-row instance).
+  // Five to eight rows over five to seven tiles per workgroup (from
+  // K = 3072): the segmented kernel's two-group form, ahead of both pairs
+  // forms.  Measured (graph-replayed, cold weights): N = 12288 K = 5120 M = 8
+  // 9.43 -> 8.14 us, N = 9216 M = 8 8.26 -> 7.20, N = 10240 M = 6 7.68 ->
+  // 7.16, N = 10240 K = 6144 M = 8 9.67 -> 8.09, N = 12288 K = 4096 M = 5
+  // 7.30 -> 6.56, and against the two subgroups at 16 MB or more, N = 14336
+  // K = 5120 M = 8 9.26 -> 8.69, M = 6 9.52 -> 8.55 (N = 10240 K = 3072 M = 8
+  // even).
+  if constexpr (MMAX > 4) {
+    if (K >= 3072u) {
+      EvenGrid eg;
+      const hipError_t e = even_grid(N, eg);
+      if (e != hipSuccess) return e;
+      if (eg.tiles >= 5u && eg.tiles <= 7u) return launch_segs<MMAX>(eg, stream, a, b, c, N, K, M);
+    }
+  }
   if constexpr (MMAX > 4) {
     const size_t lds2 = pair_lds_bytes<8, 2>(M, K);
     if (big && lds2 <= kLdsMax) {
