@@ -194,14 +194,15 @@ def test_two_to_four_rows_every_staging_tier(oracle_mod, N, K, M):
 
 
 @pytest.mark.parametrize("N,K,M", [(8, 5120, 8), (20, 1024, 5), (4104, 5120, 7), (17408, 5120, 6), (1032, 2048, 8),
-                                   (3, 5120, 6), (16392, 5120, 8), (17400, 5120, 5), (12336, 5120, 8),
-                                   (12344, 5120, 8)])
+                                   (3, 5120, 6), (16392, 5120, 8), (17400, 5120, 5), (15416, 4096, 8),
+                                   (15424, 4096, 8)])
 def test_five_to_eight_rows_tile_counts(oracle_mod, N, K, M):
     """Five to eight resident activation rows over tile counts 1, 3 (odd), 513,
     129 and N below one tile (one group of 8 waves per workgroup), and over
     2176, 2049 and 2175 tiles of matrices of 16 MB or more (two subgroups per
     workgroup, where the second walks padding tiles when it owns fewer), and
-    both sides of that 16 MB switch (N = 12336 just under, 12344 just over):
+    both sides of that 16 MB switch at eight tiles per workgroup (K = 4096,
+    N = 15416 just under, 15424 just over):
     every row bit-identical to its own M=1 launch, a canary row past M
     untouched, all columns (or a sample holding the last one) within
     tolerance of the oracle."""
