@@ -247,7 +247,7 @@ def test_segmented_kernel_tiles_and_segments(oracle_mod, N, K, M):
 
 @pytest.mark.parametrize("N,K,M", [(5120, 17408, 2), (4100, 16384, 2), (12288, 20480, 2), (20480, 16384, 2),
                                    (8192, 17408, 4), (8192, 17408, 3), (5120, 7168, 6), (4096, 7168, 5),
-                                   (5120, 6144, 7), (5120, 11264, 4), (5120, 14336, 3)])
+                                   (5120, 6144, 7), (5120, 11264, 4), (5120, 14336, 3), (7168, 6144, 7)])
 def test_segmented_kernel_extra_routes(oracle_mod, N, K, M):
     """Two rows whose activations are 64 KB or more (K >= 16384) run the
     segmented kernel's 2-row instance over two to nine tiles per workgroup
@@ -255,8 +255,8 @@ def test_segmented_kernel_extra_routes(oracle_mod, N, K, M):
     but not over ten (N = 20480 stays with the resident-activation kernel);
     three or four rows of 96 KB or more over four tiles run its 4-row
     instance (N = 8192, K = 17408); five to seven rows of 60 KB or more from
-    K = 6144 on run its 6- and 8-row instances over two or three tiles
-    (N = 5120 and 4096, K = 7168 and 6144); three or four rows of 84 KB or
+    K = 6144 on run its 6- and 8-row instances over two to four tiles
+    (N = 5120 and 4096, K = 7168 and 6144; N = 7168, four tiles); three or four rows of 84 KB or
     more over three tiles run its 4-row instance (K = 11264 and 14336).
     Every
     row bit-identical to its own M=1 launch (the resident-activation kernel),

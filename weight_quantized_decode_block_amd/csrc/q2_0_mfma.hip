@@ -1110,18 +1110,22 @@ hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32
   // even).  Five to eight rows from K = 6144 on take it from 60 KB (one pairs
   // workgroup per CU there): N = 5120 K = 7168 M = 6 8.14 -> 6.39 us, K = 6144
   // M = 7 7.64 -> 6.68, K = 8192 M = 5 8.05 -> 7.40, N = 4096 K = 7168 M = 5
-  // 6.19 -> 5.45 (K = 6144 M = 5 and N = 6144 M = 6 even); at K = 5120 the
-  // pairs kernel stays (N = 5120 M = 6 5.68 against 5.93).  Three or four
+  // 6.19 -> 5.45 (K = 6144 M = 5 and N = 6144 M = 6 even), and over four
+  // tiles N = 7168 K = 6144 M = 7 8.78 -> 7.72 (N = K = 8192 M = 8 even); at
+  // K = 5120 the pairs kernel stays (N = 5120 M = 6 5.68 against 5.93, over
+  // four tiles N = 8192 M = 8 7.29 against 7.48).  Three or four
   // rows from 84 KB on: N = 5120 K = 14336 M = 3 11.21 -> 9.61, K = 11264
   // M = 4 9.51 -> 8.99 (at 80 KB, K = 10240 M = 4, the pairs kernel stays:
   // 8.40 against 8.78).
   if constexpr (MMAX >= 4) {
     const uint64_t a_bytes = (uint64_t)M * K * 2u;
-    if (a_bytes >= (MMAX == 4 ? 84u : 96u) * 1024u || (M >= 5u && K >= 6144u && a_bytes >= 60u * 1024u)) {
+    const bool wide = M >= 5u && K >= 6144u && a_bytes >= 60u * 1024u;  // five to eight rows from K = 6144
+    if (a_bytes >= (MMAX == 4 ? 84u : 96u) * 1024u || wide) {
       EvenGrid eg;
       const hipError_t e = even_grid(N, eg);
       if (e != hipSuccess) return e;
-      if (eg.tiles >= 2u && eg.tiles <= (MMAX == 4 ? 4u : 3u)) return launch_segs<MMAX>(eg, stream, a, b, c, N, K, M);
+      if (eg.tiles >= 2u && eg.tiles <= (MMAX == 4 || wide ? 4u : 3u))
+        return launch_segs<MMAX>(eg, stream, a, b, c, N, K, M);
     }
   }
   // Two rows of 64 KB or more (K >= 16384) over two to nine tiles per
