@@ -1068,12 +1068,6 @@ hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32
   //     M = 4 12.94 -> 12.53; two subgroups (below) N = 17408 K = 5120 M = 5
   //     11.67 -> 10.97, M = 8 11.30 -> 10.61.
   //
-  // Five to eight rows of a matrix of 16 MB or more: two subgroups of 8 waves
-  // per workgroup over one copy of the activations (measured on MI355X,
-  // N = 17408, K = 5120: M = 8 12.45 -> 11.46 us, M = 5 12.54 -> 11.70; at
-  // N = K = 5120 one group stays faster, 6.74 against 7.31).  The 8-row
-  // instance serves the 6-row tier here too (the same bits; N = 17408,
-  // K = 5120, M = 6: 11.78 against 12.14 us for the 6-row instance).
   // Five to eight rows over five to seven tiles per workgroup (from
   // K = 3072): the segmented kernel's two-group form, ahead of both pairs
   // forms.  Measured (graph-replayed, cold weights): N = 12288 K = 5120 M = 8
@@ -1090,6 +1084,12 @@ hipError_t launch_mmax(const void *A, const void *B, void *C, uint32_t N, uint32
       if (eg.tiles >= 5u && eg.tiles <= 7u) return launch_segs<MMAX>(eg, stream, a, b, c, N, K, M);
     }
   }
+  // Five to eight rows of a matrix of 16 MB or more: two subgroups of 8 waves
+  // per workgroup over one copy of the activations (measured on MI355X,
+  // N = 17408, K = 5120: M = 8 12.45 -> 11.46 us, M = 5 12.54 -> 11.70; at
+  // N = K = 5120 one group stays faster, 6.74 against 7.31).  The 8-row
+  // instance serves the 6-row tier here too (the same bits; N = 17408,
+  // K = 5120, M = 6: 11.78 against 12.14 us for the 6-row instance).
   if constexpr (MMAX > 4) {
     const size_t lds2 = pair_lds_bytes<8, 2>(M, K);
     if (big && lds2 <= kLdsMax) {
